@@ -1,0 +1,83 @@
+"""Per-element scalar loops of the triangle multiplicative update.
+
+TEST INFRASTRUCTURE ONLY.  A second, independent spelling of the definition
+in ``trimul_ref`` (same readings, see that module's docstring): every sum is
+an explicit Python loop over plain floats, nothing is vectorised and no
+library routine is used, so that an index, transpose or sign mistake in the
+vectorised oracle cannot also be present here by construction.  Only for tiny
+inputs (N <= 8).
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def _ln(v, gamma, beta, eps):
+    n = len(v)
+    mu = 0.0
+    for t in v:
+        mu += t
+    mu /= n
+    var = 0.0
+    for t in v:
+        var += (t - mu) * (t - mu)
+    var /= n
+    inv = 1.0 / math.sqrt(var + eps)
+    return [(v[e] - mu) * inv * gamma[e] + beta[e] for e in range(n)]
+
+
+def _sig(t):
+    if t >= 0:
+        return 1.0 / (1.0 + math.exp(-t))
+    e = math.exp(t)
+    return e / (1.0 + e)
+
+
+def _matvec(W, v):
+    out = []
+    for row in W:
+        s = 0.0
+        for e in range(len(v)):
+            s += row[e] * v[e]
+        out.append(s)
+    return out
+
+
+def trimul_loops(z, mask, w, direction, eps=1e-5):
+    """z: nested lists [N][N][c_z]; mask: [N][N]; w: dict of nested lists.
+    Returns out as nested lists [N][N][c_z]."""
+    n = len(z)
+    W = {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()}
+    c = len(W["w_a_proj"])
+    zh = [[_ln(list(map(float, z[i][j])), W["ln_in_w"], W["ln_in_b"], eps) for j in range(n)]
+          for i in range(n)]
+    a = [[None] * n for _ in range(n)]
+    b = [[None] * n for _ in range(n)]
+    for i in range(n):
+        for j in range(n):
+            m = 1.0 if mask[i][j] else 0.0
+            ap = _matvec(W["w_a_proj"], zh[i][j])
+            ag = _matvec(W["w_a_gate"], zh[i][j])
+            bp = _matvec(W["w_b_proj"], zh[i][j])
+            bg = _matvec(W["w_b_gate"], zh[i][j])
+            a[i][j] = [m * _sig(ag[d]) * ap[d] for d in range(c)]
+            b[i][j] = [m * _sig(bg[d]) * bp[d] for d in range(c)]
+    out = [[None] * n for _ in range(n)]
+    for i in range(n):
+        for j in range(n):
+            x = []
+            for d in range(c):
+                s = 0.0
+                for k in range(n):
+                    if direction == "outgoing":
+                        s += a[i][k][d] * b[j][k][d]
+                    else:
+                        s += a[k][i][d] * b[k][j][d]
+                x.append(s)
+            nn = _ln(x, W["ln_out_w"], W["ln_out_b"], eps)
+            y = _matvec(W["w_out_proj"], nn)
+            g = _matvec(W["w_out_gate"], zh[i][j])
+            m = 1.0 if mask[i][j] else 0.0
+            out[i][j] = [m * _sig(g[e]) * y[e] for e in range(len(y))]
+    return out

@@ -1,0 +1,397 @@
+"""CPU pins of the float64 oracle.
+
+Each test fixes the oracle against something other than itself: an
+independent scalar-loop spelling, a closed form worked by hand, a library
+routine in a special case that reduces to it, or an invariant of the
+mathematics (permutation equivariance, the transpose relation between the two
+directions, mask semantics, additivity of tile partial sums).  The pages print
+no numeric example for this layer, so nothing here comes from the pages'
+numbers.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bruteforce
+from oracle.trimul_ref import array_getters
+import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def rand_weights(c_z, c, seed, random_ln=True):
+    """float64 weights for oracle-only tests (not tied to a storage dtype)."""
+    r = np.random.default_rng(seed)
+    w = {
+        "w_a_proj": r.standard_normal((c, c_z)) / math.sqrt(c_z),
+        "w_a_gate": r.standard_normal((c, c_z)) / math.sqrt(c_z),
+        "w_b_proj": r.standard_normal((c, c_z)) / math.sqrt(c_z),
+        "w_b_gate": r.standard_normal((c, c_z)) / math.sqrt(c_z),
+        "w_out_gate": r.standard_normal((c_z, c_z)) / math.sqrt(c_z),
+        "w_out_proj": r.standard_normal((c_z, c)) / math.sqrt(c),
+        "ln_in_w": 1 + 0.1 * r.standard_normal(c_z) if random_ln else np.ones(c_z),
+        "ln_in_b": 0.1 * r.standard_normal(c_z) if random_ln else np.zeros(c_z),
+        "ln_out_w": 1 + 0.1 * r.standard_normal(c) if random_ln else np.ones(c),
+        "ln_out_b": 0.1 * r.standard_normal(c) if random_ln else np.zeros(c),
+    }
+    return w
+
+
+def rand_inputs(n, c_z, seed, keep=0.8):
+    r = np.random.default_rng(seed + 1000)
+    z = r.standard_normal((n, n, c_z))
+    m = (r.random((n, n)) < keep).astype(np.uint8)
+    return z, m
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.max(np.abs(a - b)) / max(np.sqrt(np.mean(b * b)), 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# elementary pieces
+# ---------------------------------------------------------------------------
+
+def test_bf16_round_properties():
+    r = np.random.default_rng(0)
+    x = r.standard_normal(20000) * np.exp2(r.integers(-30, 30, 20000))
+    q = oracle.bf16_round(x)
+    # representable: a float32 whose low 16 bits are zero
+    q32 = q.astype(np.float32)
+    assert np.all(q32.astype(np.float64) == q)
+    assert np.all((q32.view(np.uint32) & 0xFFFF) == 0)
+    # nearest: no bf16 neighbour is closer
+    bits = q32.view(np.uint32)
+    up = ((bits + 0x10000) & 0xFFFFFFFF).astype(np.uint32).view(np.float32).astype(np.float64)
+    dn = ((bits - 0x10000) & 0xFFFFFFFF).astype(np.uint32).view(np.float32).astype(np.float64)
+    err = np.abs(x - q)
+    assert np.all(err <= np.abs(x - up))
+    assert np.all(err <= np.abs(x - dn))
+
+
+def test_bf16_round_ties_and_specials():
+    one = 1.0
+    ulp = 2.0 ** -7                      # bf16 spacing in [1, 2)
+    assert oracle.bf16_round(one + ulp / 2) == one                  # tie -> even (1.0)
+    assert oracle.bf16_round(one + 1.5 * ulp) == one + 2 * ulp      # tie -> even mantissa
+    assert oracle.bf16_round(one + ulp / 2 + 2.0 ** -40) == one + ulp
+    assert oracle.bf16_round(-(one + ulp / 2)) == -one
+    assert oracle.bf16_round(0.0) == 0.0
+    assert oracle.bf16_round(2.0 ** -133) == 2.0 ** -133            # smallest subnormal
+    assert oracle.bf16_round(3.4e38) == np.inf                      # beyond max finite
+    assert np.isnan(oracle.bf16_round(np.nan))
+
+
+def test_bf16_round_matches_torch_on_float32_inputs():
+    # torch rounds float32 -> bfloat16 to nearest-even; on float32-exact inputs the
+    # one-step float64 rounding must agree with it.
+    x = np.random.default_rng(1).standard_normal(50000).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_round(x.astype(np.float64)), t)
+
+
+def test_sigmoid():
+    t = np.linspace(-30, 30, 601)
+    ref = np.array([1.0 / (1.0 + math.exp(-v)) for v in t])
+    assert np.max(np.abs(oracle.sigmoid(t) - ref)) < 1e-15
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.sigmoid(-1000.0) == 0.0 and oracle.sigmoid(1000.0) == 1.0
+    assert np.allclose(oracle.sigmoid(t) + oracle.sigmoid(-t), 1.0, atol=1e-15)
+
+
+def test_layer_norm_closed_form():
+    v = np.array([1.0, 2.0, 3.0, 4.0])
+    # mean 2.5, biased variance 1.25
+    want = (v - 2.5) / math.sqrt(1.25 + 1e-5)
+    got = oracle.layer_norm(v, np.ones(4), np.zeros(4))
+    assert np.max(np.abs(got - want)) < 1e-15
+    g = np.array([2.0, -1.0, 0.5, 3.0])
+    b = np.array([0.1, 0.2, 0.3, 0.4])
+    assert np.max(np.abs(oracle.layer_norm(v, g, b) - (want * g + b))) < 1e-15
+    # constant vector: zero deviation, the eps branch returns beta exactly
+    assert np.array_equal(oracle.layer_norm(np.full(4, 7.0), g, b), b)
+    # shift invariance
+    r = np.random.default_rng(2).standard_normal((5, 16))
+    assert np.max(np.abs(oracle.layer_norm(r + 3.25, np.ones(16), np.zeros(16))
+                         - oracle.layer_norm(r, np.ones(16), np.zeros(16)))) < 1e-13
+
+
+def test_gate_half_and_identity_projection():
+    c = 8
+    z, m = rand_inputs(3, c, 5, keep=1.0)
+    w = rand_weights(c, c, 5)
+    w["w_a_gate"][:] = 0
+    w["w_b_gate"][:] = 0
+    w["w_a_proj"] = np.eye(c)
+    w["w_b_proj"] = 2 * np.eye(c)
+    a, b = oracle.project(z, m, w)
+    zh = oracle.layer_norm(z, w["ln_in_w"], w["ln_in_b"])
+    assert np.max(np.abs(a - 0.5 * zh)) < 1e-15
+    assert np.max(np.abs(b - zh)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# whole definition vs the scalar-loop spelling
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("n,c_z,c", [(1, 4, 4), (2, 4, 8), (3, 8, 4), (5, 6, 4), (6, 8, 8)])
+def test_vectorised_matches_bruteforce_small(direction, n, c_z, c):
+    w = rand_weights(c_z, c, 10 + n)
+    z, m = rand_inputs(n, c_z, 20 + n, keep=0.75)
+    got = oracle.trimul(z, m, w, direction)
+    want = np.array(bruteforce.trimul_loops(z.tolist(), m.tolist(), w, direction))
+    assert rel(got, want) < 1e-12
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_vectorised_matches_bruteforce_full_width(direction):
+    n, c_z, c = 4, 128, 128
+    w = rand_weights(c_z, c, 33)
+    z, m = rand_inputs(n, c_z, 34, keep=0.8)
+    got = oracle.trimul(z, m, w, direction)
+    want = np.array(bruteforce.trimul_loops(z.tolist(), m.tolist(), w, direction))
+    assert rel(got, want) < 1e-12
+
+
+def test_hand_worked_example_c2():
+    """c_z = c = 2 worked by hand.
+
+    With two channels, LN(p, q) = sign(p - q) * s * (1, -1) for
+    s = h / sqrt(h^2 + eps), h = |p - q| / 2 (gamma = 1, beta = 0).  With
+    W_ag = W_bg = 0 (gates 1/2), W_ap = diag(1, 2), W_bp = I, the operands are
+    a = zh * (1/2, 1), b = zh / 2, so outgoing x_ij = (T_ij / 4) * (1, 2) with
+    T_ij = sum_k u_ik u_jk, u = sign * s.  LN of (t, 2t) is
+    sign(t) * r * (-1, 1), r = (|t|/2) / sqrt(t^2/4 + eps).  With W_o = I,
+    W_g = 0 (gate 1/2) and mask 1: out_ij = (1/2) * sign(T) * r(T/4) * (-1, 1).
+    """
+    eps = 1e-5
+    p = np.array([[0.3, -1.2], [2.0, 0.7]])
+    q = np.array([[1.1, 0.4], [-0.5, 0.7 + 1e-3]])
+    z = np.stack([p, q], axis=-1)
+    m = np.ones((2, 2), np.uint8)
+    w = {
+        "w_a_proj": np.diag([1.0, 2.0]), "w_a_gate": np.zeros((2, 2)),
+        "w_b_proj": np.eye(2), "w_b_gate": np.zeros((2, 2)),
+        "w_out_gate": np.zeros((2, 2)), "w_out_proj": np.eye(2),
+        "ln_in_w": np.ones(2), "ln_in_b": np.zeros(2),
+        "ln_out_w": np.ones(2), "ln_out_b": np.zeros(2),
+    }
+    u = np.zeros((2, 2))
+    for i in range(2):
+        for j in range(2):
+            h = abs(p[i, j] - q[i, j]) / 2
+            u[i, j] = math.copysign(h / math.sqrt(h * h + eps), p[i, j] - q[i, j])
+    want = np.zeros((2, 2, 2))
+    for i in range(2):
+        for j in range(2):
+            T = u[i, 0] * u[j, 0] + u[i, 1] * u[j, 1]
+            t = T / 4
+            r = (abs(t) / 2) / math.sqrt(t * t / 4 + eps)
+            want[i, j] = 0.5 * math.copysign(r, t) * np.array([-1.0, 1.0])
+    got = oracle.trimul(z, m, w, "outgoing")
+    assert np.max(np.abs(got - want)) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# special cases that reduce to a library routine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_contraction_reduces_to_gram_matmul(direction):
+    """Gates 0 (sigma = 1/2), identity projections, mask 1: a = b = zh / 2, so
+    outgoing X_d = Zh_d Zh_d^T / 4 and incoming X_d = Zh_d^T Zh_d / 4 (torch.bmm)."""
+    n, c = 7, 16
+    w = rand_weights(c, c, 41)
+    for k in ("w_a_gate", "w_b_gate"):
+        w[k][:] = 0
+    w["w_a_proj"] = np.eye(c)
+    w["w_b_proj"] = np.eye(c)
+    z, _ = rand_inputs(n, c, 42)
+    m = np.ones((n, n), np.uint8)
+    _, x = oracle.trimul(z, m, w, direction, return_x=True)
+    zh = torch.from_numpy(oracle.layer_norm(z, w["ln_in_w"], w["ln_in_b"])).permute(2, 0, 1)
+    if direction == "outgoing":
+        X = torch.bmm(zh, zh.transpose(1, 2).contiguous()) / 4
+    else:
+        X = torch.bmm(zh.transpose(1, 2).contiguous(), zh) / 4
+    assert rel(x, X.permute(1, 2, 0).numpy()) < 1e-13
+
+
+def test_single_k_mask_gives_outer_product():
+    """Pair mask m_ik = [k == k0] leaves one term: x_ij = a_ik0 * b_jk0."""
+    n, c_z, c, k0 = 6, 8, 8, 2
+    w = rand_weights(c_z, c, 51)
+    z, _ = rand_inputs(n, c_z, 52)
+    m = np.zeros((n, n), np.uint8)
+    m[:, k0] = 1
+    _, x = oracle.trimul(z, m, w, "outgoing", return_x=True)
+    a, b = oracle.project(z, np.ones((n, n)), w)
+    want = a[:, k0, None, :] * b[None, :, k0, :]
+    assert rel(x, want) < 1e-13
+
+
+def test_tied_weights_gram_is_psd():
+    n, c = 9, 8
+    w = rand_weights(c, c, 61)
+    w["w_b_proj"] = w["w_a_proj"].copy()
+    w["w_b_gate"] = w["w_a_gate"].copy()
+    z, m = rand_inputs(n, c, 62, keep=0.9)
+    _, x = oracle.trimul(z, m, w, "outgoing", return_x=True)
+    for d in range(c):
+        X = x[:, :, d]
+        assert np.max(np.abs(X - X.T)) < 1e-13
+        assert np.min(np.linalg.eigvalsh((X + X.T) / 2)) > -1e-12
+
+
+def test_n1():
+    c_z, c = 8, 8
+    w = rand_weights(c_z, c, 71)
+    z, _ = rand_inputs(1, c_z, 72)
+    m = np.ones((1, 1), np.uint8)
+    o_out, x_out = oracle.trimul(z, m, w, "outgoing", return_x=True)
+    o_in, x_in = oracle.trimul(z, m, w, "incoming", return_x=True)
+    a, b = oracle.project(z, m, w)
+    assert np.max(np.abs(x_out[0, 0] - a[0, 0] * b[0, 0])) < 1e-15
+    assert np.array_equal(o_out, o_in)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_permutation_equivariance(direction):
+    n, c_z, c = 11, 8, 8
+    w = rand_weights(c_z, c, 81)
+    z, m = rand_inputs(n, c_z, 82, keep=0.8)
+    perm = np.random.default_rng(83).permutation(n)
+    out = oracle.trimul(z, m, w, direction)
+    out_p = oracle.trimul(z[np.ix_(perm, perm)], m[np.ix_(perm, perm)], w, direction)
+    assert rel(out_p, out[np.ix_(perm, perm)]) < 1e-12
+
+
+def test_transpose_relation_between_directions():
+    """incoming(z, m; W) = outgoing(z^T, m^T; W with a <-> b swapped)^T.  The
+    literal 'same weights' form holds only when the a and b weights are tied."""
+    n, c_z, c = 10, 8, 8
+    w = rand_weights(c_z, c, 91)
+    z, m = rand_inputs(n, c_z, 92, keep=0.85)
+    zt = np.swapaxes(z, 0, 1)
+    mt = m.T
+    inc = oracle.trimul(z, m, w, "incoming")
+    ws = dict(w)
+    ws["w_a_proj"], ws["w_b_proj"] = w["w_b_proj"], w["w_a_proj"]
+    ws["w_a_gate"], ws["w_b_gate"] = w["w_b_gate"], w["w_a_gate"]
+    assert rel(inc, np.swapaxes(oracle.trimul(zt, mt, ws, "outgoing"), 0, 1)) < 1e-12
+    # untied, unswapped: genuinely different
+    assert rel(inc, np.swapaxes(oracle.trimul(zt, mt, w, "outgoing"), 0, 1)) > 1e-3
+    wt = dict(w)
+    wt["w_b_proj"], wt["w_b_gate"] = w["w_a_proj"], w["w_a_gate"]
+    assert rel(oracle.trimul(z, m, wt, "incoming"),
+               np.swapaxes(oracle.trimul(zt, mt, wt, "outgoing"), 0, 1)) < 1e-12
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_masked_pairs_contribute_nothing(direction):
+    n, c_z, c = 9, 8, 8
+    w = rand_weights(c_z, c, 101)
+    z, m = rand_inputs(n, c_z, 102, keep=0.7)
+    out = oracle.trimul(z, m, w, direction)
+    assert np.all(out[m == 0] == 0)
+    z2 = z.copy()
+    z2[m == 0] = np.random.default_rng(103).standard_normal(z2[m == 0].shape) * 50
+    assert np.array_equal(oracle.trimul(z2, m, w, direction), out)
+    assert np.all(oracle.trimul(z, np.zeros_like(m), w, direction) == 0)
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_tile_partials_sum_to_full(direction):
+    n, c_z, c = 12, 8, 8
+    w = rand_weights(c_z, c, 111)
+    z, m = rand_inputs(n, c_z, 112, keep=0.85)
+    gz, gm = array_getters(z, m)
+    _, x = oracle.trimul(z, m, w, direction, return_x=True)
+    out = oracle.trimul(z, m, w, direction)
+    h = n // 2
+    chunks = [np.arange(t * 3, t * 3 + 3) for t in range(4)]
+    for r0 in (0, h):
+        for c0 in (0, h):
+            rows, cols = np.arange(r0, r0 + h), np.arange(c0, c0 + h)
+            parts = [oracle.tile_partial(gz, gm, n, w, direction, rows, cols, k) for k in chunks]
+            ring = sum(parts)
+            rotated = sum(parts[2:] + parts[:2])
+            assert np.max(np.abs(ring - x[r0:r0 + h, c0:c0 + h])) < 1e-13
+            assert np.max(np.abs(rotated - ring)) < 1e-13
+            fin = oracle.finish(ring, z[r0:r0 + h, c0:c0 + h], m[r0:r0 + h, c0:c0 + h], w)
+            assert np.max(np.abs(fin - out[r0:r0 + h, c0:c0 + h])) < 1e-13
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_sampled_and_blockwise_match_full(direction):
+    n, c_z, c = 20, 8, 8
+    w = rand_weights(c_z, c, 121)
+    z, m = rand_inputs(n, c_z, 122, keep=0.9)
+    out = oracle.trimul(z, m, w, direction)
+    rows = np.array([0, 3, 19, 7])
+    cols = np.array([19, 0, 5])
+    gz, gm = array_getters(z, m)
+    s = oracle.trimul_sampled(gz, gm, n, w, direction, rows, cols)
+    assert np.max(np.abs(s - out[np.ix_(rows, cols)])) < 1e-13
+    assert np.max(np.abs(oracle.trimul_blockwise(z, m, w, direction, block=6) - out)) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Q-mode (bf16 contraction operands)
+# ---------------------------------------------------------------------------
+
+def test_qmode_operands_are_bf16_and_contract_exactly():
+    n, c_z, c = 6, 16, 8
+    w = rand_weights(c_z, c, 131)
+    z, m = rand_inputs(n, c_z, 132, keep=0.8)
+    a, b = oracle.project(z, m, w, quant=True)
+    for t in (a, b):
+        assert np.array_equal(t.astype(np.float32).astype(np.float64), t)
+        assert np.all((t.astype(np.float32).view(np.uint32) & 0xFFFF) == 0)
+    _, xq = oracle.trimul(z, m, w, "outgoing", quant=True, return_x=True)
+    # contraction of the rounded operands, by explicit loops
+    want = np.zeros((n, n, c))
+    for i in range(n):
+        for j in range(n):
+            for k in range(n):
+                want[i, j] += a[i, k] * b[j, k]
+    assert np.max(np.abs(xq - want)) < 1e-13
+
+
+def test_qmode_is_close_to_but_not_exact():
+    wts = wl.make_weights(128, 128, seed=3, dtype="bf16")
+    w = wl.weights_f64(wts)
+    z = wl.make_pair_tensor(48, 128, 3, "bf16", "cpu").double().numpy()
+    m = np.ones((48, 48), np.uint8)
+    ex = oracle.trimul(z, m, w, "outgoing")
+    q = oracle.trimul(z, m, w, "outgoing", quant=True)
+    e = rel(q, ex)
+    assert 1e-4 < e < 6e-2
+
+
+# ---------------------------------------------------------------------------
+# stored regression fixture (written by tests/golden/make_golden.py from the
+# brute-force loops only)
+# ---------------------------------------------------------------------------
+
+def test_golden_fixture():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "trimul_n4_c6.json")
+    g = json.load(open(path))
+    w = {k: np.array(v) for k, v in g["weights"].items()}
+    z = np.array(g["z"])
+    m = np.array(g["mask"], np.uint8)
+    for d in ("outgoing", "incoming"):
+        assert rel(oracle.trimul(z, m, w, d), np.array(g["out_" + d])) < 1e-12
