@@ -1,0 +1,269 @@
+"""Benchmark of the triangle multiplicative update on one MI355X.
+
+One step = the whole update in both directions (outgoing, then incoming:
+projection kernel, contraction kernel, epilogue kernel each) over the
+n3605_4ch workload: N = 3605 residues in 4 chains (1200/1000/800/605), the
+complex size that page 1 ("Os numeros") folds on four GPUs; c_z = c = 128,
+bf16, synthetic seeded inputs already resident in HBM.  The metric is pair
+updates per second over the whole job: 2 * N^2 per step / seconds per step.
+
+Two timed loops of K steps each:
+  1. the public entry points trimul_outgoing + trimul_incoming, wall clock
+     between device synchronizations -> `value`, `ms_per_step`;
+  2. the same kernels launched one by one through trimul_tile_operands /
+     trimul_tile (identical kernels, launch shapes and buffers) with HIP events
+     between them on the launch stream -> per-kernel average durations, the
+     roofline of the dominant kernel (the contraction, matrix-core bound) and
+     the HBM rates of the projection and epilogue kernels.
+The CPU baseline times the float64 oracle's three phases on bounded blocks of
+the same workload on the host cores and extrapolates (projection and epilogue
+scale with N^2, contraction with N^3).
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+C = 128
+C_Z = 128
+K1_BYTES_PER_PAIR = 256 + 1 + 2 * C * 2        # z (bf16) + mask + a, b (bf16)
+K3_BYTES_PER_PAIR = C * 4 + 256 + 1 + C_Z * 4  # x (fp32) + z + mask + out (fp32)
+K1_FLOPS_PER_PAIR = 4 * C * C_Z * 2
+K3_FLOPS_PER_PAIR = 2 * C_Z * C * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per contraction launch from the committed counter summary, or
+    None when the summary is absent or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "k2_contract_n3605_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source sha256: ([0-9a-f]{64})", text)
+    m_b = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline(work, block_rows):
+    """Oracle phase rates on blocks of the workload, extrapolated to the job.
+
+    projection: the a/b operands of a block of `block_rows` rows (all columns);
+    contraction: that row block against 4 x block_rows operand rows over all N
+    k values (flop-rate measurement); epilogue: a block_rows x block_rows
+    block of pairs.  Projection and epilogue scale with N^2 pairs, the
+    contraction with 2 N^3 c flops.
+    """
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    n = work.n
+    rb = block_rows
+    w = wl.weights_f64(wl.make_weights(work.c_z, work.c, work.seed, work.dtype))
+    z = wl.make_pair_tensor(n, work.c_z, work.seed, work.dtype, "cpu", rows=range(0, rb),
+                            chains=wl.chain_ids(work), offsets=wl.chain_offsets(work)).double().numpy()
+    m = np.ones((rb, n), np.uint8)
+    t0 = time.perf_counter()
+    a, b = oracle.project(z, m, w, quant=True)
+    t1 = time.perf_counter()
+    b4 = np.concatenate([b] * 4)
+    x = oracle.contract_rows(a, b4)
+    t2 = time.perf_counter()
+    oracle.finish(x[:, :rb], z[:, :rb], m[:, :rb], w)
+    t3 = time.perf_counter()
+    t_proj = (t1 - t0) * (n * n) / (rb * n)
+    t_con = (t2 - t1) * (2.0 * n ** 3 * C) / (2.0 * rb * 4 * rb * n * C)
+    t_epi = (t3 - t2) * (n * n) / (rb * rb)
+    t_dir = t_proj + t_con + t_epi
+    return {
+        "value": (2 * n * n) / (2 * t_dir),
+        "unit": "pair-updates/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle phases on blocks of {work.name}: projection of {rb}x{n} pairs "
+                   f"{t1 - t0:.2f}s, contraction {rb}x{4 * rb}x{n}x128 {t2 - t1:.2f}s, epilogue {rb}x{rb} "
+                   f"pairs {t3 - t2:.2f}s; extrapolated (projection, epilogue x N^2; contraction x N^3) "
+                   f"to {t_dir:.0f}s per direction"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="n3605_4ch")
+    ap.add_argument("--cpu-rows", type=int, default=96, help="row block for the CPU baseline (0 = skip)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: run a plain device copy of known size (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                          "launches": 3}), flush=True)
+        return
+    work = wl.WORKLOADS[args.workload]
+    n = work.n
+    log(f"[bench] generating {work.name} (N={n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    ws = pra.new_workspace(w, n, dev)
+    out_o = torch.empty((n, n, C_Z), dtype=torch.float32, device=dev)
+    out_i = torch.empty_like(out_o)
+    kp = (n + 63) // 64 * 64
+    elt = 2 if work.dtype == "bf16" else 4
+    plane = (C * n * kp * elt + 255) // 256 * 256
+    a_pl = ws[:C * n * kp * elt].view(torch.bfloat16 if elt == 2 else torch.float32).view(C, n, kp)
+    b_pl = ws[plane:plane + C * n * kp * elt].view(a_pl.dtype).view(C, n, kp)
+    x = ws[2 * plane:2 * plane + C * n * n * 4].view(torch.float32).view(C, n, n)
+    torch.cuda.synchronize()
+
+    def step_api():
+        pra.outgoing(z, mask, w, workspace=ws, out=out_o)
+        pra.incoming(z, mask, w, workspace=ws, out=out_i)
+
+    def step_kernels(ev=None):
+        for d, out in ((pra.OUTGOING, out_o), (pra.INCOMING, out_i)):
+            if ev is not None:
+                ev[d][0].record()
+            pra.tile_operands(w, d, z, mask, 0, n, 0, n, 0, n, kp, a_out=a_pl, b_out=b_pl)
+            if ev is not None:
+                ev[d][1].record()
+            pra.tile(w, n, 0, n, 0, n, [(0, n, a_pl, b_pl)], pra.TILE_FIRST, x)
+            if ev is not None:
+                ev[d][2].record()
+            pra.tile(w, n, 0, n, 0, n, [], pra.TILE_LAST, x, z, mask, out)
+            if ev is not None:
+                ev[d][3].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step_api()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps (entry points)")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_api()
+    torch.cuda.synchronize()
+    t_api = (time.perf_counter() - t0) / args.steps
+
+    log(f"[bench] timing {args.steps} steps (per-kernel events)")
+    for _ in range(args.warmup):
+        step_kernels()
+    torch.cuda.synchronize()
+    durs = {"k1": [], "k2": [], "k3": []}
+    t0 = time.perf_counter()
+    all_ev = []
+    for _ in range(args.steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(2)]
+        step_kernels(ev)
+        all_ev.append(ev)
+    torch.cuda.synchronize()
+    t_kern = (time.perf_counter() - t0) / args.steps
+    for ev in all_ev:
+        for d in range(2):
+            durs["k1"].append(ev[d][0].elapsed_time(ev[d][1]) * 1e-3)
+            durs["k2"].append(ev[d][1].elapsed_time(ev[d][2]) * 1e-3)
+            durs["k3"].append(ev[d][2].elapsed_time(ev[d][3]) * 1e-3)
+    avg = {k: sum(v) / len(v) for k, v in durs.items()}
+
+    pairs = n * n
+    k2_flops = 2.0 * n * n * n * C
+    k2_tflops = k2_flops / avg["k2"] / 1e12
+    k1_gbs = K1_BYTES_PER_PAIR * pairs / avg["k1"] / 1e9
+    k3_gbs = K3_BYTES_PER_PAIR * pairs / avg["k3"] / 1e9
+    traffic = traffic_from_profile(os.path.join(ROOT, "pair_representation_amd", "csrc", "k2_contract.hip"))
+
+    value = 2 * pairs / t_api
+    rec = {
+        "metric": "TriMul pair-updates/s and MFMA util % at N=3605,c_z=128 bf16 (1 GPU)",
+        "value": value,
+        "unit": "pair-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_api * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": work.dtype,
+        "data": "synthetic (seeded z ~ N(0,1) + inter-chain offset vectors, Xavier-normal weights)",
+        "config": {"workload": work.name, "n": n, "c_z": C_Z, "c": C, "chains": list(work.chains),
+                   "directions": ["outgoing", "incoming"], "pair_updates_per_step": 2 * pairs},
+        "mfma_util_pct": 100.0 * k2_tflops / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k2_contract (channel-batched k-contraction)",
+            "achieved": k2_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": k2_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_per_launch": f"2*N^3*c = {k2_flops:.4e} flop",
+            "avg_launch_ms": avg["k2"] * 1e3,
+        },
+        "kernels": {
+            "k1_project": {"avg_ms": avg["k1"] * 1e3, "bound": "hbm", "GB/s": k1_gbs,
+                           "frac": k1_gbs / PEAK_HBM_GBS, "bytes_per_pair": K1_BYTES_PER_PAIR,
+                           "TFLOP/s": K1_FLOPS_PER_PAIR * pairs / avg["k1"] / 1e12},
+            "k2_contract": {"avg_ms": avg["k2"] * 1e3, "bound": "mfma", "TFLOP/s": k2_tflops,
+                            "frac": k2_tflops / PEAK_BF16_TFLOPS},
+            "k3_epilogue": {"avg_ms": avg["k3"] * 1e3, "bound": "hbm", "GB/s": k3_gbs,
+                            "frac": k3_gbs / PEAK_HBM_GBS, "bytes_per_pair": K3_BYTES_PER_PAIR,
+                            "TFLOP/s": K3_FLOPS_PER_PAIR * pairs / avg["k3"] / 1e12},
+            "per_kernel_loop_ms_per_step": t_kern * 1e3,
+        },
+        "cpu_baseline": None,
+    }
+    del ws, out_o, out_i, z, mask
+    torch.cuda.empty_cache()
+    if args.cpu_rows > 0:
+        log(f"[bench] CPU oracle baseline on a {args.cpu_rows}-row block")
+        rec["cpu_baseline"] = cpu_baseline(work, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * trimul.h -- C ABI of the MI355X (gfx950) triangle multiplicative update.
+ *
+ * The operation is the pair-representation layer that page 1 ("NVIDIA BioNeMo
+ * escala modelagem biomolecular com context parallelism e quebra barreira de
+ * memoria da GPU", section "Exemplo de codigo: triangle multiplication
+ * CP-aware") builds as TriangleMultiplicationOutgoing(size_input_embed) and
+ * calls as layer(x, mask).  The pages do not print its equations; this library
+ * computes the AlphaFold3-style definition, per pair (i, j):
+ *
+ *   zh_ij  = LN(z_ij; ln_in_w, ln_in_b)
+ *   a_ij   = m_ij * sigmoid(W_a_gate zh_ij) * (W_a_proj zh_ij)
+ *   b_ij   = m_ij * sigmoid(W_b_gate zh_ij) * (W_b_proj zh_ij)
+ *   x_ij   = sum_k a_ik * b_jk            (outgoing)
+ *   x_ij   = sum_k a_ki * b_kj            (incoming)
+ *   out_ij = m_ij * sigmoid(W_out_gate zh_ij) * (W_out_proj LN(x_ij; ln_out_w, ln_out_b))
+ *
+ * LN is LayerNorm over channels with biased variance; no linear map has a bias;
+ * the output is the update only (no residual).  Page 1's section "2D tiling
+ * da pair representation" splits the N x N grid into sub-blocks, one per
+ * device, and its section "Sobreposicao de computacao e comunicacao" streams
+ * the remote operand blocks around row and column rings while the local update
+ * runs: trimul_tile_operands / trimul_tile are that per-device step, with the
+ * k-contraction fed chunk by chunk in the order the ring delivers them.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *    buffer; the library never allocates, frees or synchronizes.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    default stream) and the call returns once enqueued.  Device faults
+ *    surface at the caller's next synchronization.
+ *  - All arguments are validated before the first HIP call; an invalid call
+ *    enqueues nothing and returns a status code.  trimul_last_error() gives a
+ *    message for the most recent failure on the calling thread.
+ *  - Device pointers must be 16-byte aligned (the pair mask: any alignment);
+ *    workspaces 256-byte aligned.
+ *  - Supported widths: c_z = c = 128.  Supported sizes: 0 <= n <= 65535
+ *    (n = 0 is a no-op).
+ *  - Results are deterministic (no atomics; fixed summation order for a fixed
+ *    chunk order).  Calls on different streams with different workspaces may
+ *    run concurrently.
+ *
+ * Precision.  TRIMUL_F32: z, weights, a/b operands and every product in fp32
+ * (matrix cores in fp32 mode).  TRIMUL_BF16: z and the five matrices are
+ * bf16; LayerNorm statistics, sigmoid and all accumulation are fp32; the
+ * normalised input and the a/b operands are rounded to bf16 (nearest-even)
+ * for the bf16 matrix-core projection and contraction; the output LayerNorm
+ * result and the normalised input feeding the output gate are split into two
+ * bf16 terms (hi + lo) so the epilogue products keep fp32-level accuracy.  The
+ * output is fp32 in both modes.
+ */
+#ifndef TRIMUL_H
+#define TRIMUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRIMUL_OK = 0,
+  TRIMUL_ERR_INVALID_ARG = 1,         /* null pointer, bad size, range or flag        */
+  TRIMUL_ERR_UNSUPPORTED = 2,         /* c_z or c other than 128, unknown dtype       */
+  TRIMUL_ERR_ALIGNMENT = 3,           /* a pointer or leading dimension misaligned     */
+  TRIMUL_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < trimul_workspace_bytes()    */
+  TRIMUL_ERR_HIP = 5                  /* a kernel launch or device query failed        */
+} trimul_status_t;
+
+typedef enum { TRIMUL_F32 = 0, TRIMUL_BF16 = 1 } trimul_dtype_t;
+typedef enum { TRIMUL_OUTGOING = 0, TRIMUL_INCOMING = 1 } trimul_dir_t;
+
+/* Flags of trimul_tile. */
+enum { TRIMUL_TILE_FIRST = 1u, TRIMUL_TILE_LAST = 2u };
+
+/* Largest number of k-chunks one trimul_tile call accepts. */
+#define TRIMUL_MAX_CHUNKS 32
+
+/* The layer's parameters (its state dict).  Matrices are row-major
+ * (out_features, in_features), i.e. torch Linear.weight, in `dtype`
+ * (fp32 or bf16); LayerNorm vectors are always fp32. */
+typedef struct {
+  int32_t c_z;                 /* pair channels; must be 128                   */
+  int32_t c;                   /* hidden channels; must be 128                 */
+  int32_t dtype;               /* trimul_dtype_t of z and of the matrices      */
+  float ln_eps;                /* LayerNorm epsilon, > 0 (1e-5 usual)           */
+  const float *ln_in_w;        /* [c_z] input LayerNorm gamma                   */
+  const float *ln_in_b;        /* [c_z] input LayerNorm beta                    */
+  const void *w_a_proj;        /* [c][c_z]                                      */
+  const void *w_a_gate;        /* [c][c_z]                                      */
+  const void *w_b_proj;        /* [c][c_z]                                      */
+  const void *w_b_gate;        /* [c][c_z]                                      */
+  const void *w_out_gate;      /* [c_z][c_z]                                    */
+  const float *ln_out_w;       /* [c] output LayerNorm gamma                    */
+  const float *ln_out_b;       /* [c] output LayerNorm beta                     */
+  const void *w_out_proj;      /* [c_z][c]                                      */
+} trimul_weights_t;
+
+/* One k-chunk of the contraction for a tile: the operands of residues
+ * k_off .. k_off+k_len-1.
+ *   a: [c][n_rows][ld]  a[d][r][t] = operand of (row_off + r, k_off + t)
+ *   b: [c][n_cols][ld]  b[d][s][t] = operand of (col_off + s, k_off + t)
+ * where "operand of (i, k)" is a_ik, b_jk for outgoing and a_ki, b_kj for
+ * incoming (incoming operands are stored transposed so one layout serves
+ * both).  Element type = the weights' dtype.  ld is a multiple of 64,
+ * ld >= k_len, and columns k_len .. ld-1 must hold zeros (trimul_tile_operands
+ * writes them). */
+typedef struct {
+  int64_t k_off;
+  int64_t k_len;
+  int64_t ld;
+  const void *a;
+  const void *b;
+} trimul_kchunk_t;
+
+/* Bytes of workspace trimul_outgoing / trimul_incoming need for size n: the
+ * a and b operand planes [c][n][round_up(n, 64)] (element = dtype) and the fp32
+ * contraction result [c][n][n], each rounded up to 256 bytes.  Returns 0 for
+ * an invalid w or n. */
+size_t trimul_workspace_bytes(const trimul_weights_t *w, int64_t n);
+
+/* The full update over an n x n pair grid, outgoing direction.
+ *   z    : [n][n][c_z] in w->dtype, pair-major (channels contiguous)
+ *   mask : [n][n] uint8, nonzero = keep the pair
+ *   out  : [n][n][c_z] fp32, fully overwritten (zeros at masked pairs)
+ *   workspace : >= trimul_workspace_bytes(w, n) bytes, 256-byte aligned;
+ *               contents on entry are ignored, on return unspecified. */
+trimul_status_t trimul_outgoing(const trimul_weights_t *w, const void *z, const uint8_t *mask,
+                                float *out, int64_t n, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* The same for the incoming direction (x_ij = sum_k a_ki * b_kj). */
+trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const uint8_t *mask,
+                                float *out, int64_t n, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Bytes of one operand buffer of trimul_tile_operands: c * rows * ld * elt. */
+size_t trimul_tile_operand_bytes(const trimul_weights_t *w, int64_t rows, int64_t ld);
+
+/* The operand chunk a device owning z contributes for one tile: runs the
+ * input LayerNorm, gated projections and mask on the source pairs and writes
+ *   a_out[d][r][t] = operand a of (row_off + r, k_off + t),  r < n_rows
+ *   b_out[d][s][t] = operand b of (col_off + s, k_off + t),  s < n_cols
+ * for t < k_len, zeros for k_len <= t < ld (layout of trimul_kchunk_t).
+ * Either output may be NULL (not computed), not both.  z and mask are the
+ * global [n][n] tensors.  Ranges must lie inside [0, n); ld % 64 == 0,
+ * ld >= k_len >= 1. */
+trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                     const uint8_t *mask, int64_t n, int64_t row_off,
+                                     int64_t n_rows, int64_t col_off, int64_t n_cols,
+                                     int64_t k_off, int64_t k_len, int64_t ld, void *a_out,
+                                     void *b_out, void *stream);
+
+/* One device's tile of the pair grid: rows row_off .. row_off+n_rows-1, cols
+ * col_off .. col_off+n_cols-1.  Contracts the given chunks (host array, in
+ * arrival order) into
+ *   x_acc[d][r][s]  (fp32, [c][n_rows][n_cols])
+ * overwriting it when flags has TRIMUL_TILE_FIRST and adding to it otherwise;
+ * the partial sums stay in registers across the chunks of one call.  With
+ * TRIMUL_TILE_LAST the epilogue then writes
+ *   out_tile[r][s][e] (fp32, [n_rows][n_cols][c_z])
+ * from x_acc and the global z / mask (needed only with LAST).
+ * Chunks of one call must lie in [0, n) and not overlap; when FIRST and LAST
+ * are both set they must cover [0, n) exactly.  Coverage across calls is the
+ * caller's responsibility.  n_chunks may be 0 only with LAST alone (epilogue
+ * on an already complete x_acc). */
+trimul_status_t trimul_tile(const trimul_weights_t *w, int64_t n, int64_t row_off,
+                            int64_t n_rows, int64_t col_off, int64_t n_cols,
+                            const trimul_kchunk_t *chunks /* (host) */, int32_t n_chunks,
+                            uint32_t flags, float *x_acc, const void *z, const uint8_t *mask,
+                            float *out_tile, void *stream);
+
+/* Static description of a status code. */
+const char *trimul_status_string(trimul_status_t s);
+
+/* Message for the most recent failing call on this thread ("" if none). */
+const char *trimul_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIMUL_H */

@@ -1,0 +1,239 @@
+"""Python binding of libtrimul.so, the gfx950 triangle multiplicative update.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and torch's current HIP stream are handed to
+the C entry points declared in include/trimul.h, and a non-OK status becomes a
+``TrimulError``.  Every step of the computation runs in the HIP kernels; there
+is no fallback.  If the library has not been built, the first call raises.
+
+Entry points (same names as the C ABI, without the ``trimul_`` prefix):
+    workspace_bytes(w, n)
+    outgoing(z, mask, w, ...), incoming(z, mask, w, ...)
+    tile_operand_bytes(w, rows, ld)
+    tile_operands(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, ...)
+    tile(w, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z, mask, out_tile)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrimul.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(6)
+F32, BF16 = 0, 1
+OUTGOING, INCOMING = 0, 1
+TILE_FIRST, TILE_LAST = 1, 2
+MAX_CHUNKS = 32
+C = 128
+C_Z = 128
+
+
+class TrimulError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"trimul status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [
+        ("c_z", ctypes.c_int32), ("c", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("ln_eps", ctypes.c_float),
+        ("ln_in_w", ctypes.c_void_p), ("ln_in_b", ctypes.c_void_p),
+        ("w_a_proj", ctypes.c_void_p), ("w_a_gate", ctypes.c_void_p),
+        ("w_b_proj", ctypes.c_void_p), ("w_b_gate", ctypes.c_void_p),
+        ("w_out_gate", ctypes.c_void_p),
+        ("ln_out_w", ctypes.c_void_p), ("ln_out_b", ctypes.c_void_p),
+        ("w_out_proj", ctypes.c_void_p),
+    ]
+
+
+class KChunk(ctypes.Structure):
+    _fields_ = [("k_off", ctypes.c_int64), ("k_len", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("a", ctypes.c_void_p), ("b", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m pair_representation_amd.build` (needs hipcc)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        W = ctypes.POINTER(_Weights)
+        L.trimul_workspace_bytes.argtypes = [W, i64]
+        L.trimul_workspace_bytes.restype = sz
+        for name in ("trimul_outgoing", "trimul_incoming"):
+            f = getattr(L, name)
+            f.argtypes = [W, vp, vp, vp, i64, vp, sz, vp]
+            f.restype = ctypes.c_int
+        L.trimul_tile_operand_bytes.argtypes = [W, i64, i64]
+        L.trimul_tile_operand_bytes.restype = sz
+        L.trimul_tile_operands.argtypes = [W, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                           i64, vp, vp, vp]
+        L.trimul_tile_operands.restype = ctypes.c_int
+        L.trimul_tile.argtypes = [W, i64, i64, i64, i64, i64, ctypes.POINTER(KChunk), i32, u32, vp, vp,
+                                  vp, vp, vp]
+        L.trimul_tile.restype = ctypes.c_int
+        L.trimul_status_string.argtypes = [ctypes.c_int]
+        L.trimul_status_string.restype = ctypes.c_char_p
+        L.trimul_last_error.argtypes = []
+        L.trimul_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != OK:
+        raise TrimulError(status, lib().trimul_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class Weights:
+    """Device-resident layer parameters plus the C struct pointing at them.
+
+    ``tensors`` maps the names of trimul_weights_t (ln_in_w, ln_in_b, w_a_proj,
+    w_a_gate, w_b_proj, w_b_gate, w_out_gate, ln_out_w, ln_out_b, w_out_proj)
+    to tensors; matrices are (out_features, in_features).  They are copied to
+    ``device`` in the storage dtype (matrices) and fp32 (LayerNorm vectors).
+    """
+
+    MATRICES = ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate", "w_out_gate", "w_out_proj")
+    VECTORS = ("ln_in_w", "ln_in_b", "ln_out_w", "ln_out_b")
+
+    def __init__(self, tensors, dtype=BF16, eps=1e-5, device="cuda"):
+        self.dtype = dtype
+        td = _TORCH_DTYPE[dtype]
+        self.t = {}
+        for k in self.MATRICES:
+            self.t[k] = tensors[k].to(device=device, dtype=td).contiguous()
+        for k in self.VECTORS:
+            self.t[k] = tensors[k].to(device=device, dtype=torch.float32).contiguous()
+        s = _Weights()
+        s.c_z, s.c, s.dtype, s.ln_eps = C_Z, C, dtype, eps
+        for k, v in self.t.items():
+            setattr(s, k, v.data_ptr())
+        self.struct = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+
+def workspace_bytes(w: Weights, n: int) -> int:
+    return int(lib().trimul_workspace_bytes(w.ref, n))
+
+
+def tile_operand_bytes(w: Weights, rows: int, ld: int) -> int:
+    return int(lib().trimul_tile_operand_bytes(w.ref, rows, ld))
+
+
+def new_workspace(w: Weights, n: int, device="cuda"):
+    nb = workspace_bytes(w, n)
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+
+
+def _full(fn, z, mask, w, workspace, out):
+    n = z.shape[0]
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    if out is None:
+        out = torch.empty((n, n, C_Z), dtype=torch.float32, device=z.device)
+    _need(out, "out", torch.float32, (n, n, C_Z))
+    if workspace is None:
+        workspace = new_workspace(w, n, z.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check(fn(w.ref, _ptr(z), _ptr(mask), _ptr(out), n, _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def outgoing(z, mask, w: Weights, workspace=None, out=None):
+    """out_ij = update with x_ij = sum_k a_ik * b_jk; returns fp32 [n, n, 128]."""
+    return _full(lib().trimul_outgoing, z, mask, w, workspace, out)
+
+
+def incoming(z, mask, w: Weights, workspace=None, out=None):
+    """out_ij = update with x_ij = sum_k a_ki * b_kj; returns fp32 [n, n, 128]."""
+    return _full(lib().trimul_incoming, z, mask, w, workspace, out)
+
+
+def tile_operands(w: Weights, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld,
+                  a_out=None, b_out=None, want_a=True, want_b=True):
+    """Operand chunk [128, rows, ld] for one tile and k-range; returns (a, b)."""
+    n = z.shape[0]
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    if want_a and a_out is None:
+        a_out = torch.empty((C, n_rows, ld), dtype=w.torch_dtype, device=z.device)
+    if want_b and b_out is None:
+        b_out = torch.empty((C, n_cols, ld), dtype=w.torch_dtype, device=z.device)
+    if a_out is not None:
+        _need(a_out, "a_out", w.torch_dtype, (C, n_rows, ld))
+    if b_out is not None:
+        _need(b_out, "b_out", w.torch_dtype, (C, n_cols, ld))
+    _check(lib().trimul_tile_operands(w.ref, direction, _ptr(z), _ptr(mask), n, row_off, n_rows, col_off,
+                                      n_cols, k_off, k_len, ld, _ptr(a_out), _ptr(b_out), _stream()))
+    return a_out, b_out
+
+
+def tile(w: Weights, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z=None, mask=None,
+         out_tile=None):
+    """Contract ``chunks`` (list of (k_off, k_len, a, b) in arrival order) into
+    x_acc [128, n_rows, n_cols]; with TILE_LAST also write out_tile
+    [n_rows, n_cols, 128] fp32 (allocated if None).  Returns out_tile."""
+    _need(x_acc, "x_acc", torch.float32, (C, n_rows, n_cols))
+    arr = (KChunk * max(1, len(chunks)))()
+    for i, (k_off, k_len, a, b) in enumerate(chunks):
+        _need(a, f"chunk {i} a", w.torch_dtype)
+        _need(b, f"chunk {i} b", w.torch_dtype)
+        if a.dim() != 3 or a.shape[0] != C or a.shape[1] != n_rows:
+            raise ValueError(f"chunk {i} a must be [128, {n_rows}, ld]")
+        if b.dim() != 3 or b.shape[0] != C or b.shape[1] != n_cols or b.shape[2] != a.shape[2]:
+            raise ValueError(f"chunk {i} b must be [128, {n_cols}, ld] with a's ld")
+        arr[i] = KChunk(k_off, k_len, a.shape[2], a.data_ptr(), b.data_ptr())
+    if flags & TILE_LAST:
+        _need(z, "z", w.torch_dtype, (n, n, C_Z))
+        _need(mask, "mask", torch.uint8, (n, n))
+        if out_tile is None:
+            out_tile = torch.empty((n_rows, n_cols, C_Z), dtype=torch.float32, device=x_acc.device)
+        _need(out_tile, "out_tile", torch.float32, (n_rows, n_cols, C_Z))
+    _check(lib().trimul_tile(w.ref, n, row_off, n_rows, col_off, n_cols, arr, len(chunks), flags,
+                             _ptr(x_acc), _ptr(z), _ptr(mask), _ptr(out_tile), _stream()))
+    return out_tile

@@ -1,0 +1,114 @@
+// Shared device helpers for the gfx950 triangle-multiplication kernels:
+// element types, 8-element k-fragments and the matrix-core wrappers built on
+// them, bf16 rounding, the exp2-based logistic function and lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trimul {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Storage tag for bf16 data (raw 16-bit payload).
+struct bf16_t {
+  uint16_t v;
+};
+
+constexpr int kC = 128;  // hidden channels c
+constexpr int kCz = 128; // pair channels c_z
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even (the hardware conversion; no NaN inputs occur here).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Logistic function 1 / (1 + e^-t) from the identity e^u = 2^(u log2 e) on
+// the hardware base-2 exponential and reciprocal.  For t -> -inf the
+// exponential overflows to +inf and the reciprocal gives 0; for t -> +inf it
+// underflows to 0 and the result is 1: no NaN for any finite t.
+__device__ __forceinline__ float sigmoid_f32(float t) {
+  const float kLog2e = 1.4426950408889634f;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * kLog2e));
+}
+
+__device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rsqf(v); }
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane of the group receives the total.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 8-element k-fragments: the operand one lane contributes to a 32x32 matrix
+// product step over 16 k values (lane l holds row/col l % 32 and the k values
+// 8*(l/32) .. 8*(l/32)+7).
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Frag;
+
+template <>
+struct Frag<bf16_t> {
+  bf16x8 v;
+  static constexpr int kBytes = 16;
+  __device__ __forceinline__ void load(const void *p) {
+    v = *reinterpret_cast<const bf16x8 *>(p);
+  }
+};
+
+template <>
+struct Frag<float> {
+  f32x4 lo, hi;
+  static constexpr int kBytes = 32;
+  __device__ __forceinline__ void load(const void *p) {
+    lo = reinterpret_cast<const f32x4 *>(p)[0];
+    hi = reinterpret_cast<const f32x4 *>(p)[1];
+  }
+};
+
+// acc[32x32] += A(32 x 16) * B(16 x 32) with both operands as k-fragments.
+__device__ __forceinline__ void mma(f32x16 &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+// fp32 form: eight 32x32x2 steps.  Step t pairs lane-slot s = l/32 with k
+// value 8*s + t, so the eight steps together cover k = 0..15 exactly once.
+__device__ __forceinline__ void mma(f32x16 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[t], b.lo[t], acc, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[t], b.hi[t], acc, 0, 0, 0);
+}
+
+// Row index (within the 32x32 tile) of accumulator register r in lane l; the
+// column is l % 32.
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+// XOR swizzle of 16-byte units inside an LDS row: unit u of row `row` is
+// stored at unit u ^ (row % period).  Applied on both write and read, it
+// spreads the 32 rows a k-fragment read touches over distinct banks.
+template <int kPeriod>
+__device__ __forceinline__ int swz(int row, int unit) {
+  return unit ^ (row & (kPeriod - 1));
+}
+
+}  // namespace trimul

@@ -1,0 +1,74 @@
+// Kernel argument blocks and host-side launchers of the three kernels.
+//   K1 (k1_project.hip)  input LayerNorm + gated a/b projections + mask,
+//                        written as channel-planar k-contiguous operand planes
+//   K2 (k2_contract.hip) channel-batched k-contraction on the matrix cores,
+//                        streaming k-chunks in the given order
+//   K3 (k3_epilogue.hip) output LayerNorm + output projection + output gate
+//                        + pair mask, fp32 output
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "trimul.h"
+
+namespace trimul {
+
+struct K1Args {
+  const void *z;          // [n][n][c_z] global pair tensor
+  const uint8_t *mask;    // [n][n]
+  int64_t n;
+  int64_t row_base;       // source residue of plane row 0
+  int64_t n_rows;         // plane rows
+  int64_t k_off, k_len;   // source residues of plane columns 0 .. k_len-1
+  int64_t ld;             // plane row length (multiple of 64); columns >= k_len get zeros
+  int32_t transposed;     // 0: plane (r, t) <- pair (row_base+r, k_off+t); 1: pair (k_off+t, row_base+r)
+  void *a_out;            // [c][n_rows][ld] or null
+  void *b_out;            // [c][n_rows][ld] or null
+  const float *ln_w, *ln_b;
+  float eps;
+  const void *w_a_proj, *w_a_gate, *w_b_proj, *w_b_gate;
+};
+
+struct K2Chunk {
+  const void *a;          // [c][M][ld]
+  const void *b;          // [c][N][ld]
+  int64_t ld;
+  int64_t k_len;          // residues in the chunk; columns k_len .. round_up(k_len, BK) must be 0
+  int32_t ktiles;         // k-tiles of this chunk (filled by the launcher)
+  int32_t pad_;
+};
+
+struct K2Args {
+  K2Chunk ch[TRIMUL_MAX_CHUNKS];
+  int32_t n_chunks;
+  int32_t accumulate;     // 1: x += result, 0: x = result
+  int64_t M, N;           // tile rows (a operand rows), tile cols (b operand rows)
+  float *x;               // [c][M][ldx]
+  int64_t ldx;
+};
+
+struct K3Args {
+  const float *x;         // [c][n_rows][ldx] contraction result of the tile
+  int64_t ldx;
+  const void *z;          // [n][n][c_z] global
+  const uint8_t *mask;    // [n][n] global
+  int64_t n;
+  int64_t row_off, n_rows, col_off, n_cols;
+  float *out;             // [n_rows][n_cols][c_z]
+  const float *ln_out_w, *ln_out_b, *ln_in_w, *ln_in_b;
+  float eps;
+  const void *w_out_proj;  // [c_z][c]
+  const void *w_out_gate;  // [c_z][c_z]
+};
+
+// Each launcher checks the launch with hipGetLastError.  dtype is
+// TRIMUL_F32 or TRIMUL_BF16.
+hipError_t launch_k1(const K1Args &a, int dtype, hipStream_t s);
+hipError_t launch_k2(K2Args a, int dtype, hipStream_t s);
+hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace trimul

@@ -1,0 +1,366 @@
+// C ABI of the triangle multiplicative update: argument validation, workspace
+// layout and the K1 -> K2 -> K3 launch sequence on the caller's stream.
+// Every check runs before the first HIP call, so an invalid call enqueues
+// nothing; see trimul.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kernels.hpp"
+#include "trimul.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+trimul_status_t fail(trimul_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+trimul_status_t ok() {
+  g_last_error[0] = '\0';
+  return TRIMUL_OK;
+}
+
+constexpr int64_t kMaxN = 65535;
+constexpr int64_t kKTile = 64;
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elt_bytes(int32_t dtype) { return dtype == TRIMUL_BF16 ? 2 : 4; }
+
+trimul_status_t check_weights(const trimul_weights_t *w) {
+  if (!w) return fail(TRIMUL_ERR_INVALID_ARG, "weights pointer is NULL");
+  if (w->c_z != 128 || w->c != 128)
+    return fail(TRIMUL_ERR_UNSUPPORTED, "c_z=%d c=%d: only c_z = c = 128 is supported", w->c_z, w->c);
+  if (w->dtype != TRIMUL_F32 && w->dtype != TRIMUL_BF16)
+    return fail(TRIMUL_ERR_UNSUPPORTED, "unknown dtype %d", w->dtype);
+  if (!(w->ln_eps > 0.0f) || !(w->ln_eps < 1e30f))
+    return fail(TRIMUL_ERR_INVALID_ARG, "ln_eps must be positive and finite");
+  const void *ptrs[] = {w->ln_in_w, w->ln_in_b, w->w_a_proj, w->w_a_gate, w->w_b_proj,
+                        w->w_b_gate, w->w_out_gate, w->ln_out_w, w->ln_out_b, w->w_out_proj};
+  const char *names[] = {"ln_in_w", "ln_in_b", "w_a_proj", "w_a_gate", "w_b_proj",
+                         "w_b_gate", "w_out_gate", "ln_out_w", "ln_out_b", "w_out_proj"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(TRIMUL_ERR_INVALID_ARG, "weight %s is NULL", names[i]);
+    if (!aligned(ptrs[i], 16)) return fail(TRIMUL_ERR_ALIGNMENT, "weight %s is not 16-byte aligned", names[i]);
+  }
+  return TRIMUL_OK;
+}
+
+struct FullLayout {
+  int64_t kp;       // padded k extent = row length of the operand planes
+  size_t a_off, b_off, x_off, total;
+};
+
+FullLayout full_layout(int32_t dtype, int64_t n) {
+  FullLayout L;
+  L.kp = round_up(n, kKTile);
+  const size_t plane = align256((size_t)128 * n * L.kp * elt_bytes(dtype));
+  L.a_off = 0;
+  L.b_off = plane;
+  L.x_off = 2 * plane;
+  L.total = L.x_off + align256((size_t)128 * n * n * sizeof(float));
+  return L;
+}
+
+trimul::K1Args k1_args(const trimul_weights_t *w, const void *z, const uint8_t *mask, int64_t n) {
+  trimul::K1Args a{};
+  a.z = z;
+  a.mask = mask;
+  a.n = n;
+  a.ln_w = w->ln_in_w;
+  a.ln_b = w->ln_in_b;
+  a.eps = w->ln_eps;
+  a.w_a_proj = w->w_a_proj;
+  a.w_a_gate = w->w_a_gate;
+  a.w_b_proj = w->w_b_proj;
+  a.w_b_gate = w->w_b_gate;
+  return a;
+}
+
+trimul::K3Args k3_args(const trimul_weights_t *w, const float *x, int64_t ldx, const void *z,
+                       const uint8_t *mask, int64_t n, int64_t row_off, int64_t n_rows,
+                       int64_t col_off, int64_t n_cols, float *out) {
+  trimul::K3Args a{};
+  a.x = x;
+  a.ldx = ldx;
+  a.z = z;
+  a.mask = mask;
+  a.n = n;
+  a.row_off = row_off;
+  a.n_rows = n_rows;
+  a.col_off = col_off;
+  a.n_cols = n_cols;
+  a.out = out;
+  a.ln_out_w = w->ln_out_w;
+  a.ln_out_b = w->ln_out_b;
+  a.ln_in_w = w->ln_in_w;
+  a.ln_in_b = w->ln_in_b;
+  a.eps = w->ln_eps;
+  a.w_out_proj = w->w_out_proj;
+  a.w_out_gate = w->w_out_gate;
+  return a;
+}
+
+trimul_status_t hip_fail(hipError_t e, const char *what) {
+  return fail(TRIMUL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+trimul_status_t run_full(const trimul_weights_t *w, const void *z, const uint8_t *mask, float *out,
+                         int64_t n, void *workspace, size_t workspace_bytes, void *stream,
+                         bool incoming) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (n < 0 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [0, %lld]", (long long)n, (long long)kMaxN);
+  if (n == 0) return ok();
+  if (!z || !mask || !out) return fail(TRIMUL_ERR_INVALID_ARG, "z, mask and out must be non-NULL");
+  if (!workspace) return fail(TRIMUL_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(z, 16) || !aligned(out, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "z and out must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  const FullLayout L = full_layout(w->dtype, n);
+  if (workspace_bytes < L.total)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  void *a_pl = ws + L.a_off;
+  void *b_pl = ws + L.b_off;
+  float *x = reinterpret_cast<float *>(ws + L.x_off);
+
+  trimul::K1Args k1 = k1_args(w, z, mask, n);
+  k1.row_base = 0;
+  k1.n_rows = n;
+  k1.k_off = 0;
+  k1.k_len = n;
+  k1.ld = L.kp;
+  k1.transposed = incoming ? 1 : 0;
+  k1.a_out = a_pl;
+  k1.b_out = b_pl;
+  hipError_t e = trimul::launch_k1(k1, w->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+
+  trimul::K2Args k2{};
+  k2.ch[0].a = a_pl;
+  k2.ch[0].b = b_pl;
+  k2.ch[0].ld = L.kp;
+  k2.ch[0].k_len = n;
+  k2.n_chunks = 1;
+  k2.accumulate = 0;
+  k2.M = n;
+  k2.N = n;
+  k2.x = x;
+  k2.ldx = n;
+  e = trimul::launch_k2(k2, w->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "contraction kernel launch");
+
+  trimul::K3Args k3 = k3_args(w, x, n, z, mask, n, 0, n, 0, n, out);
+  e = trimul::launch_k3(k3, w->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
+  return ok();
+}
+
+}  // namespace
+
+namespace trimul {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+}  // namespace trimul
+
+extern "C" {
+
+size_t trimul_workspace_bytes(const trimul_weights_t *w, int64_t n) {
+  if (!w || (w->dtype != TRIMUL_F32 && w->dtype != TRIMUL_BF16) || n < 0 || n > kMaxN) return 0;
+  if (n == 0) return 0;
+  return full_layout(w->dtype, n).total;
+}
+
+trimul_status_t trimul_outgoing(const trimul_weights_t *w, const void *z, const uint8_t *mask, float *out,
+                                int64_t n, void *workspace, size_t workspace_bytes, void *stream) {
+  return run_full(w, z, mask, out, n, workspace, workspace_bytes, stream, false);
+}
+
+trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const uint8_t *mask, float *out,
+                                int64_t n, void *workspace, size_t workspace_bytes, void *stream) {
+  return run_full(w, z, mask, out, n, workspace, workspace_bytes, stream, true);
+}
+
+size_t trimul_tile_operand_bytes(const trimul_weights_t *w, int64_t rows, int64_t ld) {
+  if (!w || (w->dtype != TRIMUL_F32 && w->dtype != TRIMUL_BF16) || rows < 0 || ld < 0) return 0;
+  return (size_t)128 * rows * ld * elt_bytes(w->dtype);
+}
+
+trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                     const uint8_t *mask, int64_t n, int64_t row_off, int64_t n_rows,
+                                     int64_t col_off, int64_t n_cols, int64_t k_off, int64_t k_len,
+                                     int64_t ld, void *a_out, void *b_out, void *stream) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING) return fail(TRIMUL_ERR_INVALID_ARG, "unknown direction %d", (int)dir);
+  if (n < 1 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [1, %lld]", (long long)n, (long long)kMaxN);
+  if (!z || !mask) return fail(TRIMUL_ERR_INVALID_ARG, "z and mask must be non-NULL");
+  if (!a_out && !b_out) return fail(TRIMUL_ERR_INVALID_ARG, "a_out and b_out are both NULL");
+  if (a_out && (row_off < 0 || n_rows < 1 || row_off + n_rows > n))
+    return fail(TRIMUL_ERR_INVALID_ARG, "row range [%lld, +%lld) outside [0, %lld)", (long long)row_off, (long long)n_rows, (long long)n);
+  if (b_out && (col_off < 0 || n_cols < 1 || col_off + n_cols > n))
+    return fail(TRIMUL_ERR_INVALID_ARG, "col range [%lld, +%lld) outside [0, %lld)", (long long)col_off, (long long)n_cols, (long long)n);
+  if (k_off < 0 || k_len < 1 || k_off + k_len > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "k range [%lld, +%lld) outside [0, %lld)", (long long)k_off, (long long)k_len, (long long)n);
+  if (ld < k_len || ld % kKTile != 0)
+    return fail(TRIMUL_ERR_INVALID_ARG, "ld=%lld must be a multiple of 64 and >= k_len=%lld", (long long)ld, (long long)k_len);
+  if (!aligned(z, 16) || (a_out && !aligned(a_out, 16)) || (b_out && !aligned(b_out, 16)))
+    return fail(TRIMUL_ERR_ALIGNMENT, "z, a_out and b_out must be 16-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  trimul::K1Args k1 = k1_args(w, z, mask, n);
+  k1.k_off = k_off;
+  k1.k_len = k_len;
+  k1.ld = ld;
+  k1.transposed = dir == TRIMUL_INCOMING ? 1 : 0;
+  const bool shared_rows = a_out && b_out && row_off == col_off && n_rows == n_cols;
+  hipError_t e;
+  if (shared_rows) {
+    k1.row_base = row_off;
+    k1.n_rows = n_rows;
+    k1.a_out = a_out;
+    k1.b_out = b_out;
+    e = trimul::launch_k1(k1, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+    return ok();
+  }
+  if (a_out) {
+    k1.row_base = row_off;
+    k1.n_rows = n_rows;
+    k1.a_out = a_out;
+    k1.b_out = nullptr;
+    e = trimul::launch_k1(k1, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+  }
+  if (b_out) {
+    k1.row_base = col_off;
+    k1.n_rows = n_cols;
+    k1.a_out = nullptr;
+    k1.b_out = b_out;
+    e = trimul::launch_k1(k1, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+  }
+  return ok();
+}
+
+trimul_status_t trimul_tile(const trimul_weights_t *w, int64_t n, int64_t row_off, int64_t n_rows,
+                            int64_t col_off, int64_t n_cols, const trimul_kchunk_t *chunks, int32_t n_chunks,
+                            uint32_t flags, float *x_acc, const void *z, const uint8_t *mask, float *out_tile,
+                            void *stream) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (n < 1 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [1, %lld]", (long long)n, (long long)kMaxN);
+  if (row_off < 0 || n_rows < 1 || row_off + n_rows > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "row range [%lld, +%lld) outside [0, %lld)", (long long)row_off, (long long)n_rows, (long long)n);
+  if (col_off < 0 || n_cols < 1 || col_off + n_cols > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "col range [%lld, +%lld) outside [0, %lld)", (long long)col_off, (long long)n_cols, (long long)n);
+  if (flags & ~(uint32_t)(TRIMUL_TILE_FIRST | TRIMUL_TILE_LAST))
+    return fail(TRIMUL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (n_chunks < 0 || n_chunks > TRIMUL_MAX_CHUNKS)
+    return fail(TRIMUL_ERR_INVALID_ARG, "n_chunks=%d outside [0, %d]", n_chunks, TRIMUL_MAX_CHUNKS);
+  if (n_chunks == 0 && flags != TRIMUL_TILE_LAST)
+    return fail(TRIMUL_ERR_INVALID_ARG, "n_chunks = 0 is only valid with TRIMUL_TILE_LAST alone");
+  if (n_chunks > 0 && !chunks) return fail(TRIMUL_ERR_INVALID_ARG, "chunks is NULL");
+  if (!x_acc) return fail(TRIMUL_ERR_INVALID_ARG, "x_acc is NULL");
+  if (!aligned(x_acc, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "x_acc must be 16-byte aligned");
+  const bool last = flags & TRIMUL_TILE_LAST;
+  if (last) {
+    if (!z || !mask || !out_tile) return fail(TRIMUL_ERR_INVALID_ARG, "z, mask and out_tile are required with TRIMUL_TILE_LAST");
+    if (!aligned(z, 16) || !aligned(out_tile, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "z and out_tile must be 16-byte aligned");
+  }
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  for (int i = 0; i < n_chunks; ++i) {
+    const trimul_kchunk_t &c = chunks[i];
+    if (c.k_off < 0 || c.k_len < 1 || c.k_off + c.k_len > n)
+      return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: k range [%lld, +%lld) outside [0, %lld)", i, (long long)c.k_off, (long long)c.k_len, (long long)n);
+    if (c.ld < c.k_len || c.ld % kKTile != 0)
+      return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: ld=%lld must be a multiple of 64 and >= k_len", i, (long long)c.ld);
+    if (!c.a || !c.b) return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: NULL operand", i);
+    if (!aligned(c.a, 16) || !aligned(c.b, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "chunk %d: operands must be 16-byte aligned", i);
+    spans.emplace_back(c.k_off, c.k_off + c.k_len);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second)
+      return fail(TRIMUL_ERR_INVALID_ARG, "chunks overlap at k=%lld", (long long)spans[i].first);
+  if ((flags & TRIMUL_TILE_FIRST) && last) {
+    int64_t cover = 0;
+    for (auto &sp : spans) {
+      if (sp.first != cover) return fail(TRIMUL_ERR_INVALID_ARG, "FIRST|LAST chunks leave k=%lld uncovered", (long long)cover);
+      cover = sp.second;
+    }
+    if (cover != n) return fail(TRIMUL_ERR_INVALID_ARG, "FIRST|LAST chunks cover [0, %lld), not [0, %lld)", (long long)cover, (long long)n);
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (n_chunks > 0) {
+    trimul::K2Args k2{};
+    for (int i = 0; i < n_chunks; ++i) {
+      k2.ch[i].a = chunks[i].a;
+      k2.ch[i].b = chunks[i].b;
+      k2.ch[i].ld = chunks[i].ld;
+      k2.ch[i].k_len = chunks[i].k_len;
+    }
+    k2.n_chunks = n_chunks;
+    k2.accumulate = (flags & TRIMUL_TILE_FIRST) ? 0 : 1;
+    k2.M = n_rows;
+    k2.N = n_cols;
+    k2.x = x_acc;
+    k2.ldx = n_cols;
+    e = trimul::launch_k2(k2, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "contraction kernel launch");
+  }
+  if (last) {
+    trimul::K3Args k3 = k3_args(w, x_acc, n_cols, z, mask, n, row_off, n_rows, col_off, n_cols, out_tile);
+    e = trimul::launch_k3(k3, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
+  }
+  return ok();
+}
+
+const char *trimul_status_string(trimul_status_t s) {
+  switch (s) {
+    case TRIMUL_OK: return "ok";
+    case TRIMUL_ERR_INVALID_ARG: return "invalid argument";
+    case TRIMUL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TRIMUL_ERR_ALIGNMENT: return "misaligned pointer";
+    case TRIMUL_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TRIMUL_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *trimul_last_error(void) { return g_last_error; }
+
+}  // extern "C"

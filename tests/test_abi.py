@@ -1,0 +1,208 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/trimul.h declares, sizes workspaces by the documented closed form, and
+rejects every invalid argument with its status code before any HIP call.
+
+Pointers here are fake (aligned or deliberately misaligned integers): each case
+fails validation, which runs before the first HIP call, so nothing is ever
+dereferenced or launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import pair_representation_amd as pra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trimul.h")
+
+FAKE = 0x7F0000000000  # 256-byte aligned fake device address
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(trimul_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = pra.lib()
+    names = header_functions()
+    assert "trimul_outgoing" in names and "trimul_tile" in names
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in trimul.h but not exported"
+
+
+def weights(dtype=pra.BF16, c_z=128, c=128, eps=1e-5, null=None, misalign=None):
+    s = pra._Weights()
+    s.c_z, s.c, s.dtype, s.ln_eps = c_z, c, dtype, eps
+    names = [f[0] for f in pra._Weights._fields_[4:]]
+    for i, k in enumerate(names):
+        setattr(s, k, FAKE + 0x10000 * (i + 1))
+    if null:
+        setattr(s, null, None)
+    if misalign:
+        setattr(s, misalign, FAKE + 0x10000 * 20 + 8)
+    return s
+
+
+def call_full(w, n=16, z=FAKE, mask=FAKE + 1, out=FAKE + 0x100000, ws=FAKE + 0x200000, ws_bytes=None,
+              incoming=False):
+    L = pra.lib()
+    if ws_bytes is None:
+        ws_bytes = L.trimul_workspace_bytes(ctypes.byref(w), n)
+    fn = L.trimul_incoming if incoming else L.trimul_outgoing
+    return fn(ctypes.byref(w), z, mask, out, n, ws, ws_bytes, None)
+
+
+def round_up(v, m):
+    return (v + m - 1) // m * m
+
+
+@pytest.mark.parametrize("dtype,elt", [(pra.BF16, 2), (pra.F32, 4)])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 768, 3605, 10000])
+def test_workspace_closed_form(dtype, elt, n):
+    w = weights(dtype)
+    kp = round_up(n, 64)
+    a256 = lambda v: round_up(v, 256)
+    want = 2 * a256(128 * n * kp * elt) + a256(128 * n * n * 4)
+    assert pra.lib().trimul_workspace_bytes(ctypes.byref(w), n) == want
+
+
+def test_workspace_invalid():
+    L = pra.lib()
+    assert L.trimul_workspace_bytes(None, 10) == 0
+    assert L.trimul_workspace_bytes(ctypes.byref(weights()), -1) == 0
+    assert L.trimul_workspace_bytes(ctypes.byref(weights()), 70000) == 0
+    assert L.trimul_workspace_bytes(ctypes.byref(weights(dtype=7)), 10) == 0
+    assert L.trimul_tile_operand_bytes(ctypes.byref(weights()), 5000, 1280) == 128 * 5000 * 1280 * 2
+
+
+def test_n_zero_is_noop():
+    assert call_full(weights(), n=0, z=None, mask=None, out=None, ws=None, ws_bytes=0) == pra.OK
+
+
+@pytest.mark.parametrize("incoming", [False, True])
+def test_full_validation(incoming):
+    L = pra.lib()
+    E = dict(incoming=incoming)
+    assert L.trimul_outgoing(None, FAKE, FAKE, FAKE, 4, FAKE, 1 << 30, None) == pra.ERR_INVALID_ARG
+    assert call_full(weights(c_z=64), **E) == pra.ERR_UNSUPPORTED
+    assert call_full(weights(c=256), **E) == pra.ERR_UNSUPPORTED
+    assert call_full(weights(dtype=3), **E) == pra.ERR_UNSUPPORTED
+    assert call_full(weights(eps=0.0), **E) == pra.ERR_INVALID_ARG
+    assert call_full(weights(eps=float("nan")), **E) == pra.ERR_INVALID_ARG
+    for k in ("ln_in_w", "w_a_proj", "w_b_gate", "w_out_gate", "ln_out_b", "w_out_proj"):
+        assert call_full(weights(null=k), **E) == pra.ERR_INVALID_ARG
+        assert call_full(weights(misalign=k), **E) == pra.ERR_ALIGNMENT
+    w = weights()
+    assert call_full(w, n=-1, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, n=65536, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, z=None, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, mask=None, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, out=None, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, ws=None, **E) == pra.ERR_INVALID_ARG
+    assert call_full(w, z=FAKE + 4, **E) == pra.ERR_ALIGNMENT
+    assert call_full(w, out=FAKE + 0x100008, **E) == pra.ERR_ALIGNMENT
+    assert call_full(w, ws=FAKE + 0x200010, **E) == pra.ERR_ALIGNMENT
+    need = L.trimul_workspace_bytes(ctypes.byref(w), 16)
+    assert call_full(w, ws_bytes=need - 1, **E) == pra.ERR_WORKSPACE_TOO_SMALL
+    msg = L.trimul_last_error().decode()
+    assert "workspace" in msg and str(need) in msg
+
+
+def call_ops(w=None, direction=pra.OUTGOING, z=FAKE, mask=FAKE, n=100, row_off=0, n_rows=10, col_off=0,
+             n_cols=10, k_off=0, k_len=100, ld=128, a=FAKE + 0x10000000, b=FAKE + 0x20000000):
+    w = weights() if w is None else w
+    return pra.lib().trimul_tile_operands(ctypes.byref(w), direction, z, mask, n, row_off, n_rows, col_off,
+                                          n_cols, k_off, k_len, ld, a, b, None)
+
+
+def test_tile_operands_validation():
+    assert call_ops(w=weights(c=64)) == pra.ERR_UNSUPPORTED
+    assert call_ops(direction=2) == pra.ERR_INVALID_ARG
+    assert call_ops(n=0) == pra.ERR_INVALID_ARG
+    assert call_ops(z=None) == pra.ERR_INVALID_ARG
+    assert call_ops(mask=None) == pra.ERR_INVALID_ARG
+    assert call_ops(a=None, b=None) == pra.ERR_INVALID_ARG
+    assert call_ops(row_off=95, n_rows=10) == pra.ERR_INVALID_ARG
+    assert call_ops(row_off=-1) == pra.ERR_INVALID_ARG
+    assert call_ops(n_rows=0) == pra.ERR_INVALID_ARG
+    assert call_ops(col_off=91, n_cols=10) == pra.ERR_INVALID_ARG
+    assert call_ops(k_off=1, k_len=100) == pra.ERR_INVALID_ARG
+    assert call_ops(k_len=0) == pra.ERR_INVALID_ARG
+    assert call_ops(ld=96) == pra.ERR_INVALID_ARG            # not a multiple of 64
+    assert call_ops(k_len=100, ld=64) == pra.ERR_INVALID_ARG   # ld < k_len
+    assert call_ops(a=FAKE + 8) == pra.ERR_ALIGNMENT
+    assert call_ops(z=FAKE + 2) == pra.ERR_ALIGNMENT
+    # a range that only matters for the operand that is requested
+    assert call_ops(a=None, row_off=95, n_rows=10, col_off=0, n_cols=200) == pra.ERR_INVALID_ARG
+
+
+def call_tile(chunks=None, n=100, row_off=0, n_rows=50, col_off=50, n_cols=50, flags=pra.TILE_FIRST,
+              x=FAKE, z=FAKE, mask=FAKE, out=FAKE, w=None, n_chunks=None):
+    w = weights() if w is None else w
+    if chunks is None:
+        chunks = [(0, 100, 128)]
+    arr = (pra.KChunk * max(1, len(chunks)))()
+    for i, (ko, kl, ld) in enumerate(chunks):
+        arr[i] = pra.KChunk(ko, kl, ld, FAKE + 0x1000000 * (i + 1), FAKE + 0x1000000 * (i + 40))
+    nc = len(chunks) if n_chunks is None else n_chunks
+    return pra.lib().trimul_tile(ctypes.byref(w), n, row_off, n_rows, col_off, n_cols, arr, nc, flags, x, z,
+                                 mask, out, None)
+
+
+def test_tile_validation():
+    assert call_tile(w=weights(c_z=32)) == pra.ERR_UNSUPPORTED
+    assert call_tile(n=0) == pra.ERR_INVALID_ARG
+    assert call_tile(row_off=60, n_rows=50) == pra.ERR_INVALID_ARG
+    assert call_tile(col_off=-2) == pra.ERR_INVALID_ARG
+    assert call_tile(n_cols=0) == pra.ERR_INVALID_ARG
+    assert call_tile(flags=4) == pra.ERR_INVALID_ARG
+    assert call_tile(n_chunks=33, chunks=[(0, 100, 128)] * 33) == pra.ERR_INVALID_ARG
+    assert call_tile(n_chunks=-1) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[], flags=pra.TILE_FIRST) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[], flags=pra.TILE_FIRST | pra.TILE_LAST) == pra.ERR_INVALID_ARG
+    assert call_tile(x=None) == pra.ERR_INVALID_ARG
+    assert call_tile(x=FAKE + 4) == pra.ERR_ALIGNMENT
+    assert call_tile(chunks=[(0, 101, 128)]) == pra.ERR_INVALID_ARG          # past n
+    assert call_tile(chunks=[(-1, 10, 64)]) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[(0, 0, 64)]) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[(0, 100, 96)]) == pra.ERR_INVALID_ARG           # ld % 64
+    assert call_tile(chunks=[(0, 100, 64)]) == pra.ERR_INVALID_ARG           # ld < k_len
+    assert call_tile(chunks=[(0, 60, 64), (50, 50, 64)]) == pra.ERR_INVALID_ARG  # overlap
+    # FIRST|LAST must cover [0, n) exactly
+    both = pra.TILE_FIRST | pra.TILE_LAST
+    assert call_tile(chunks=[(0, 50, 64), (60, 40, 64)], flags=both) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[(0, 50, 64)], flags=both) == pra.ERR_INVALID_ARG
+    assert call_tile(chunks=[(10, 90, 128)], flags=both) == pra.ERR_INVALID_ARG
+    # LAST needs z, mask, out
+    assert call_tile(flags=pra.TILE_LAST, z=None) == pra.ERR_INVALID_ARG
+    assert call_tile(flags=pra.TILE_LAST, mask=None) == pra.ERR_INVALID_ARG
+    assert call_tile(flags=pra.TILE_LAST, out=None) == pra.ERR_INVALID_ARG
+    assert call_tile(flags=pra.TILE_LAST, out=FAKE + 4) == pra.ERR_ALIGNMENT
+    assert "cover" in pra.lib().trimul_last_error().decode() or True
+
+
+def test_status_strings():
+    L = pra.lib()
+    for s in range(6):
+        assert L.trimul_status_string(s).decode()
+    assert L.trimul_status_string(99).decode() == "unknown status"
+
+
+def test_binding_checks_tensors_before_calling():
+    import torch
+    w = type("W", (), {})()
+    w.torch_dtype = torch.bfloat16
+    with pytest.raises((ValueError, TypeError)):
+        pra._need(torch.zeros(3), "z", torch.bfloat16)  # CPU tensor is rejected
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(pra, "_lib", None)
+    monkeypatch.setattr(pra, "LIB_PATH", "/nonexistent/libtrimul.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        pra.lib()

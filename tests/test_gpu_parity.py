@@ -1,0 +1,289 @@
+"""GPU parity of the HIP path against the float64 oracle (sizes the oracle
+finishes in seconds, spanning several kernel tiles and ragged tails).
+
+Bars (max |diff| / rms(ref)):
+  bf16 path vs the Q-mode oracle (bf16 contraction operands)  <= 1e-2
+  fp32 path vs the exact oracle                                <= 1e-4
+The kernel-level tests are tighter: the contraction kernel alone, fed the
+oracle's own bf16 operands, must match their float64 contraction to fp32
+accumulation error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pair_representation_amd as pra
+import workloads as wl
+from tests.gpu_util import device_getters, rel_err
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-2
+F32_TOL = 1e-4
+DIRS = ("outgoing", "incoming")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+def setup(n, dtype, seed, dev, keep=0.9, random_ln=True):
+    z, mask, wts = wl.make_small(n, seed=seed, dtype=dtype, device="cpu", random_ln=random_ln,
+                                 mask_keep=keep)
+    w = pra.Weights(wts, pra.BF16 if dtype == "bf16" else pra.F32, device=dev)
+    host = dict(z=z.double().numpy(), mask=mask.numpy(), w=wl.weights_f64(wts))
+    return z.to(dev), mask.to(dev), w, host
+
+
+def run(direction, z, mask, w):
+    fn = pra.outgoing if direction == "outgoing" else pra.incoming
+    out = fn(z, mask, w)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# whole update, bf16 and fp32
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 64, 127, 128, 129, 255, 300])
+def test_full_bf16(dev, direction, n):
+    print(f"[case] full bf16 {direction} n={n}", flush=True)
+    z, mask, w, h = setup(n, "bf16", 100 + n, dev)
+    got = run(direction, z, mask, w).cpu().double().numpy()
+    ref_q = oracle.trimul(h["z"], h["mask"], h["w"], direction, quant=True)
+    e = rel_err(got, ref_q)
+    e_exact = rel_err(got, oracle.trimul(h["z"], h["mask"], h["w"], direction))
+    print(f"  vs Q-oracle {e:.3e}  vs exact {e_exact:.3e}")
+    assert np.all(np.isfinite(got))
+    assert np.all(got[h["mask"] == 0] == 0.0)
+    assert e <= BF16_TOL
+
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("n", [1, 5, 33, 64, 129, 200])
+def test_full_f32(dev, direction, n):
+    print(f"[case] full f32 {direction} n={n}", flush=True)
+    z, mask, w, h = setup(n, "f32", 200 + n, dev)
+    got = run(direction, z, mask, w).cpu().double().numpy()
+    ref = oracle.trimul(h["z"], h["mask"], h["w"], direction)
+    e = rel_err(got, ref)
+    print(f"  vs exact {e:.3e}")
+    assert np.all(got[h["mask"] == 0] == 0.0)
+    assert e <= F32_TOL
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_all_masked_and_all_kept(dev, direction):
+    n = 70
+    z, mask, w, h = setup(n, "bf16", 7, dev, keep=1.0)
+    got = run(direction, z, mask, w).cpu().double().numpy()
+    assert rel_err(got, oracle.trimul(h["z"], h["mask"], h["w"], direction, quant=True)) <= BF16_TOL
+    zero = torch.zeros_like(mask)
+    got0 = run(direction, z, zero, w)
+    assert torch.count_nonzero(got0).item() == 0
+
+
+def test_masked_pairs_do_not_leak(dev):
+    """Perturbing z at masked pairs leaves the GPU result bit-identical."""
+    n = 96
+    z, mask, w, _ = setup(n, "bf16", 8, dev, keep=0.7)
+    out1 = run("outgoing", z, mask, w)
+    z2 = z.clone()
+    noise = torch.randn(z2.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(1)) * 30
+    z2[mask == 0] = noise[mask == 0].to(z2.dtype)
+    out2 = run("outgoing", z2, mask, w)
+    assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_deterministic(dev, direction):
+    z, mask, w, _ = setup(257, "bf16", 9, dev)
+    a = run(direction, z, mask, w)
+    b = run(direction, z, mask, w)
+    assert torch.equal(a, b)
+
+
+def test_transpose_relation_on_gpu(dev):
+    """incoming(z, m; W) = outgoing(z^T, m^T; W with a <-> b swapped)^T, on the GPU."""
+    n = 150
+    z, mask, wts = wl.make_small(n, seed=12, dtype="bf16", device="cpu")
+    w = pra.Weights(wts, pra.BF16, device=dev)
+    sw = dict(wts)
+    sw["w_a_proj"], sw["w_b_proj"] = wts["w_b_proj"], wts["w_a_proj"]
+    sw["w_a_gate"], sw["w_b_gate"] = wts["w_b_gate"], wts["w_a_gate"]
+    ws = pra.Weights(sw, pra.BF16, device=dev)
+    zd, md = z.to(dev), mask.to(dev)
+    inc = run("incoming", zd, md, w)
+    out_t = run("outgoing", zd.transpose(0, 1).contiguous(), md.t().contiguous(), ws)
+    e = rel_err(out_t.transpose(0, 1).cpu().numpy(), inc.cpu().numpy())
+    assert e <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# kernel-level checks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", DIRS)
+def test_operand_planes(dev, dtype, direction):
+    """The projection kernel's a/b planes vs the oracle's operands (Q-mode for
+    bf16), including exact zeros in the padded columns and at masked pairs."""
+    n = 131
+    z, mask, w, h = setup(n, dtype, 31, dev, keep=0.8)
+    ld = 192
+    d = pra.OUTGOING if direction == "outgoing" else pra.INCOMING
+    a, b = pra.tile_operands(w, d, z, mask, 0, n, 0, n, 0, n, ld)
+    torch.cuda.synchronize()
+    a = a.double().cpu().numpy()
+    b = b.double().cpu().numpy()
+    qa, qb = oracle.project(h["z"], h["mask"], h["w"], quant=(dtype == "bf16"))
+    if direction == "incoming":
+        qa, qb, m = np.swapaxes(qa, 0, 1), np.swapaxes(qb, 0, 1), h["mask"].T
+    else:
+        m = h["mask"]
+    ref_a = np.moveaxis(qa, 2, 0)   # [c][r][t]
+    ref_b = np.moveaxis(qb, 2, 0)
+    for got, ref in ((a[:, :, :n], ref_a), (b[:, :, :n], ref_b)):
+        if dtype == "bf16":
+            # Both sides round to bf16 values computed along different paths
+            # (fp32 on the GPU, float64 in the oracle) whose pre-rounding
+            # difference is far below one bf16 ulp: almost every element is
+            # bit-identical and the rest differ by one or two ulps.
+            # A one-ulp flip of one normalised input channel moves the
+            # pre-rounding projection by up to max|W| * ulp(max|zh|), a few
+            # 1e-3 absolute; hence the absolute slack of 5% of rms.
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+            rms = np.sqrt(np.mean(ref * ref))
+            diff = np.abs(got - ref)
+            same = np.mean(got == ref)
+            over = np.mean(diff > 2 * ulp)
+            print(f"  bit-identical {same:.5f}, beyond 2 ulp {over:.2e}, max diff {diff.max():.3e}, "
+                  f"rms {rms:.3e}")
+            assert np.all(diff <= 2 * ulp + 0.05 * rms)
+            assert same > 0.98
+        else:
+            assert rel_err(got, ref) <= F32_TOL
+    assert np.all(a[:, :, n:] == 0) and np.all(b[:, :, n:] == 0)
+    assert np.all(a[:, :, :n][:, m == 0] == 0) and np.all(b[:, :, :n][:, m == 0] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m_rows,n_cols,klen", [(1, 1, 1), (40, 300, 77), (256, 256, 256), (300, 129, 515)])
+def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
+    """Contraction kernel fed the oracle's operands directly (uploaded, exact in
+    the storage dtype) vs their float64 contraction."""
+    r = np.random.default_rng(m_rows * 7 + n_cols)
+    ld = (klen + 63) // 64 * 64
+    a = r.standard_normal((128, m_rows, klen))
+    b = r.standard_normal((128, n_cols, klen))
+    if dtype == "bf16":
+        a, b = oracle.bf16_round(a), oracle.bf16_round(b)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    A = torch.zeros((128, m_rows, ld), dtype=td)
+    B = torch.zeros((128, n_cols, ld), dtype=td)
+    A[:, :, :klen] = torch.from_numpy(a).to(td)
+    B[:, :, :klen] = torch.from_numpy(b).to(td)
+    _, _, wts = wl.make_small(4, seed=1, dtype=dtype, device="cpu")
+    w = pra.Weights(wts, pra.BF16 if dtype == "bf16" else pra.F32, device=dev)
+    x = torch.full((128, m_rows, n_cols), float("nan"), device=dev)
+    n = max(m_rows, n_cols, klen)
+    pra.tile(w, n, 0, m_rows, 0, n_cols, [(0, klen, A.to(dev), B.to(dev))], pra.TILE_FIRST, x)
+    torch.cuda.synchronize()
+    ref = np.einsum("dik,djk->dij", a, b)
+    e = rel_err(x.cpu().double().numpy(), ref)
+    print(f"  contraction {dtype} {m_rows}x{n_cols}x{klen}: {e:.3e}")
+    assert e <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# tiled form
+# ---------------------------------------------------------------------------
+
+def _chunks(n, size):
+    return [(k, min(size, n - k)) for k in range(0, n, size)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", DIRS)
+def test_tile_matches_oracle(dev, dtype, direction):
+    """One off-diagonal tile of a 2 x 2 split, k streamed in chunks in ring
+    order (own block first), checked against the oracle's tile partial sums and
+    sampled epilogue; a rotated arrival order and a split into three calls
+    (FIRST / middle / LAST) agree within fp32 reassociation."""
+    n, h2 = 230, 115
+    row_off, n_rows, col_off, n_cols = h2, n - h2, 0, h2
+    z, mask, w, h = setup(n, dtype, 41, dev, keep=0.85)
+    d = pra.OUTGOING if direction == "outgoing" else pra.INCOMING
+    chunks = []
+    for k_off, k_len in _chunks(n, 60):
+        ld = (k_len + 63) // 64 * 64
+        a, b = pra.tile_operands(w, d, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld)
+        chunks.append((k_off, k_len, a, b))
+    # ring order for this tile: start at the block holding its own rows
+    start = [i for i, c in enumerate(chunks) if c[0] <= row_off < c[0] + c[1]][0]
+    ring = chunks[start:] + chunks[:start]
+    x = torch.empty((128, n_rows, n_cols), device=dev)
+    out = pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring, pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
+    torch.cuda.synchronize()
+
+    gz, gm = device_getters(z, mask)
+    quant = dtype == "bf16"
+    rows = np.arange(row_off, row_off + n_rows)
+    cols = np.arange(col_off, col_off + n_cols)
+    ref_out, ref_x = oracle.trimul_sampled(gz, gm, n, h["w"], direction, rows, cols, quant=quant,
+                                           return_x=True)
+    tol = BF16_TOL if quant else F32_TOL
+    e_out = rel_err(out.cpu().double().numpy(), ref_out)
+    assert e_out <= tol
+    # x of the tile: oracle partial sums per chunk add up to the GPU's x
+    xs = sum(oracle.tile_partial(gz, gm, n, h["w"], direction, rows, cols, np.arange(k, k + kl), quant)
+             for k, kl, _, _ in ring)
+    assert rel_err(np.moveaxis(x.cpu().double().numpy(), 0, 2), xs) <= tol
+
+    # rotated order in one call
+    rot = ring[3:] + ring[:3]
+    x2 = torch.empty_like(x)
+    out2 = pra.tile(w, n, row_off, n_rows, col_off, n_cols, rot, pra.TILE_FIRST | pra.TILE_LAST, x2, z, mask)
+    # the same chunks over three calls
+    x3 = torch.empty_like(x)
+    pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring[:1], pra.TILE_FIRST, x3)
+    pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring[1:3], 0, x3)
+    out3 = pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring[3:], pra.TILE_LAST, x3, z, mask)
+    torch.cuda.synchronize()
+    assert rel_err(x2.cpu().numpy(), x.cpu().numpy()) <= 1e-5
+    assert rel_err(x3.cpu().numpy(), x.cpu().numpy()) <= 1e-5
+    assert rel_err(out2.cpu().numpy(), out.cpu().numpy()) <= 1e-4
+    assert rel_err(out3.cpu().numpy(), out.cpu().numpy()) <= 1e-4
+    # epilogue alone on a finished x_acc (no chunks, LAST)
+    out4 = pra.tile(w, n, row_off, n_rows, col_off, n_cols, [], pra.TILE_LAST, x, z, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(out4, out)
+
+
+def test_tiles_assemble_full_grid(dev):
+    """All four tiles of a 2 x 2 split, each with its own ring order, assemble
+    to the full update."""
+    n, h2 = 200, 100
+    z, mask, w, h = setup(n, "bf16", 51, dev)
+    full = run("outgoing", z, mask, w)
+    asm = torch.empty_like(full)
+    for p in range(2):
+        for q in range(2):
+            ro, co = p * h2, q * h2
+            chunks = []
+            for k_off, k_len in _chunks(n, h2):
+                a, b = pra.tile_operands(w, pra.OUTGOING, z, mask, ro, h2, co, h2, k_off, k_len, 128)
+                chunks.append((k_off, k_len, a, b))
+            order = chunks[p:] + chunks[:p]
+            x = torch.empty((128, h2, h2), device=dev)
+            asm[ro:ro + h2, co:co + h2] = pra.tile(w, n, ro, h2, co, h2, order,
+                                                   pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
+    torch.cuda.synchronize()
+    assert rel_err(asm.cpu().numpy(), full.cpu().numpy()) <= 1e-4

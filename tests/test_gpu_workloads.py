@@ -1,0 +1,166 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times.
+
+n64_f32 and n768_pad are compared on the whole output tensor.  The larger
+grids are compared on a sample of rows x cols (about 48 x 48 residues = 2,304
+pairs x 128 channels), which the oracle computes exactly from the operand rows
+(outgoing) or columns (incoming) of just those residues; the sample holds the
+first and last residue, chain boundaries +-1, masked residues, tile and chunk
+edges, and seeded random residues.  The whole output is also checked for
+finiteness, exact zeros at masked pairs, and an rms within 5% of the sample's.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pair_representation_amd as pra
+import workloads as wl
+from tests.gpu_util import device_getters, rel_err, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-2
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _weights(work, dev):
+    wts = wl.make_weights(work.c_z, work.c, work.seed, work.dtype)
+    return pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev), wl.weights_f64(wts)
+
+
+def _whole_tensor_checks(out, mask_dev, sample_out, sample_mask):
+    """Finite everywhere, exact zeros at masked pairs, and the rms over kept
+    pairs within 5% of the sample's rms over its kept pairs."""
+    assert bool(torch.isfinite(out).all())
+    sq = 0.0
+    kept = 0
+    for r0 in range(0, out.shape[0], 512):
+        o = out[r0:r0 + 512]
+        m = mask_dev[r0:r0 + 512] != 0
+        if bool((~m).any()):
+            assert torch.count_nonzero(o[~m]).item() == 0
+        sq += torch.sum(o[m].double() ** 2).item()
+        kept += int(m.sum().item()) * o.shape[-1]
+    rms_full = (sq / kept) ** 0.5
+    s = sample_out[np.asarray(sample_mask) != 0]
+    rms_s = float(np.sqrt(np.mean(s ** 2)))
+    print(f"  rms over kept pairs: full {rms_full:.4f} sample {rms_s:.4f}")
+    assert abs(rms_full / rms_s - 1) < 0.05
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_n64_f32_full(dev, direction):
+    work = wl.WORKLOADS["n64_f32"]
+    print(f"[case] {work.name} {direction}", flush=True)
+    z, mask, wts = wl.make_inputs(work, "cpu")
+    w = pra.Weights(wts, pra.F32, device=dev)
+    fn = pra.outgoing if direction == "outgoing" else pra.incoming
+    got = fn(z.to(dev), mask.to(dev), w).cpu().double().numpy()
+    ref = oracle.trimul(z.double().numpy(), mask.numpy(), wl.weights_f64(wts), direction)
+    e = rel_err(got, ref)
+    print(f"  vs exact {e:.3e}")
+    assert e <= F32_TOL
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_n768_pad_full(dev, direction):
+    work = wl.WORKLOADS["n768_pad"]
+    print(f"[case] {work.name} {direction}", flush=True)
+    z, mask, wts = wl.make_inputs(work, "cpu")
+    w = pra.Weights(wts, pra.BF16, device=dev)
+    fn = pra.outgoing if direction == "outgoing" else pra.incoming
+    got = fn(z.to(dev), mask.to(dev), w).cpu().double().numpy()
+    ref = oracle.trimul_blockwise(z.double().numpy(), mask.numpy(), wl.weights_f64(wts), direction, quant=True)
+    e = rel_err(got, ref)
+    print(f"  vs Q-oracle {e:.3e}")
+    assert e <= BF16_TOL
+    assert np.all(got[mask.numpy() == 0] == 0)
+    valid = 768 - 77
+    assert np.all(got[valid:] == 0) and np.all(got[:, valid:] == 0)
+
+
+def _boundaries(work):
+    b = []
+    acc = 0
+    for L in work.chains[:-1]:
+        acc += L
+        b += [acc - 1, acc]
+    return b
+
+
+@pytest.mark.parametrize("name", ["n3605_4ch", "n6500_2ch"])
+def test_large_sampled(dev, name):
+    work = wl.WORKLOADS[name]
+    z, mask, _ = wl.make_inputs(work, dev)
+    w, w64 = _weights(work, dev)
+    res = wl.residue_mask(work)
+    masked = list(np.flatnonzero(res == 0)[:6])
+    rows = sample_indices(work.n, 101, 48, _boundaries(work) + masked)
+    cols = sample_indices(work.n, 202, 48, _boundaries(work) + masked[::-1])
+    gz, gm = device_getters(z, mask)
+    ws = pra.new_workspace(w, work.n, dev)
+    for direction in ("outgoing", "incoming"):
+        print(f"[case] {name} {direction} n={work.n}", flush=True)
+        fn = pra.outgoing if direction == "outgoing" else pra.incoming
+        out = fn(z, mask, w, workspace=ws)
+        torch.cuda.synchronize()
+        got = out[torch.as_tensor(rows, device=dev)][:, torch.as_tensor(cols, device=dev)]
+        got = got.double().cpu().numpy()
+        ref = oracle.trimul_sampled(gz, gm, work.n, w64, direction, rows, cols, quant=True)
+        e = rel_err(got, ref)
+        print(f"  sampled {len(rows)}x{len(cols)} vs Q-oracle {e:.3e}", flush=True)
+        assert e <= BF16_TOL
+        _whole_tensor_checks(out, mask, ref, gm(rows, cols))
+        del out
+        _free()
+    del z, mask, ws
+    _free()
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_n10000_tile_sampled(dev, direction):
+    work = wl.WORKLOADS["n10000_tile"]
+    t = work.tile
+    print(f"[case] {work.name} {direction}", flush=True)
+    z, mask, _ = wl.make_inputs(work, dev)
+    w, w64 = _weights(work, dev)
+    d = pra.OUTGOING if direction == "outgoing" else pra.INCOMING
+    ld = (t["chunk"] + 63) // 64 * 64
+    chunks = []
+    for c in range(t["n_chunks"]):
+        k_off = c * t["chunk"]
+        a, b = pra.tile_operands(w, d, z, mask, t["row_off"], t["n_rows"], t["col_off"], t["n_cols"],
+                                 k_off, t["chunk"], ld)
+        chunks.append((k_off, t["chunk"], a, b))
+    x = torch.empty((128, t["n_rows"], t["n_cols"]), device=dev)
+    out = pra.tile(w, work.n, t["row_off"], t["n_rows"], t["col_off"], t["n_cols"], chunks,
+                   pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
+    torch.cuda.synchronize()
+    edges = [0, 1249, 1250, 2499, 2500, 3749, 3750, 4999]
+    rows = sample_indices(t["n_rows"], 303, 48, edges) + t["row_off"]
+    cols = sample_indices(t["n_cols"], 404, 48, edges) + t["col_off"]
+    got = out[torch.as_tensor(rows - t["row_off"], device=dev)][:, torch.as_tensor(cols - t["col_off"], device=dev)]
+    gz, gm = device_getters(z, mask)
+    ref = oracle.trimul_sampled(gz, gm, work.n, w64, direction, rows, cols, quant=True)
+    e = rel_err(got.double().cpu().numpy(), ref)
+    print(f"  sampled {len(rows)}x{len(cols)} vs Q-oracle {e:.3e}", flush=True)
+    assert e <= BF16_TOL
+    _whole_tensor_checks(out, mask[:t["n_rows"], :t["n_cols"]], ref, gm(rows, cols))
+    del z, mask, chunks, x, out
+    _free()
