@@ -7,12 +7,17 @@
 // Work-group tile BM x BN of one channel, four waves in a 2 x 2 layout, each
 // wave a (BM/2) x (BN/2) block of 32 x 32 matrix-core accumulators.  The
 // k-loop walks the chunks in the order given (a ring's delivery order) and,
-// inside each chunk, BK-wide k-tiles.  Global -> register -> LDS staging is
-// double-buffered: the loads of k-tile t+1 are in flight while k-tile t is on
-// the matrix cores, with one barrier per k-tile.  LDS rows are XOR-swizzled in
-// 16-byte units so the k-fragment reads of 32 consecutive rows are free of
-// bank conflicts.  Partial sums stay in registers across all chunks; the
-// result is written (or added) once.
+// inside each chunk, BK-wide k-tiles.
+//
+// Operand staging: buffer loads that write LDS directly (no register
+// staging), two LDS stages, one barrier per k-tile: the loads of k-tile t+1
+// are in flight while k-tile t is on the matrix cores.  Each load instruction
+// fills 1 KB of LDS (64 lanes x 16 bytes at consecutive addresses), so the
+// XOR swizzle of 16-byte units inside a row (unit u of row r stored at
+// u ^ ((r / 2) % 8)) is applied on the global side: a lane fetches the
+// logical unit that belongs in its LDS slot.  Rows past the end of the operand fall outside
+// the buffer's range and read as zeros.  k-fragments are read from LDS one
+// 16-wide k step ahead of the matrix-core instructions that consume them.
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
@@ -28,6 +33,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T, int BM, int BN, int BK>
 struct K2Cfg {
@@ -37,13 +45,19 @@ struct K2Cfg {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MT = WM / 32, NT = WN / 32;
   static constexpr int KS = BK / 16;           // 16-wide k steps per k-tile
-  static constexpr int UPF = Frag<T>::kBytes / 16;  // units per fragment
-  static constexpr int A_LD = BM * RU / kThreads;   // 16-byte loads per thread
-  static constexpr int B_LD = BN * RU / kThreads;
+  static constexpr int A_I = BM * RU / kThreads;    // 1 KB load instructions per wave (A)
+  static constexpr int B_I = BN * RU / kThreads;
   static constexpr int STAGE = (BM + BN) * ROWB;
   static_assert(RU == 8, "LDS rows are 8 units wide");
-  static_assert(A_LD * kThreads == BM * RU && B_LD * kThreads == BN * RU, "load split");
+  static_assert(A_I * kThreads == BM * RU && B_I * kThreads == BN * RU, "load split");
 };
+
+// Physical 16-byte unit of logical unit u in LDS row r.  A 128-byte row is
+// half of the 256-byte window the 64 LDS banks cover, and a 16-byte-per-lane
+// read serves 16 lanes per cycle: 16 consecutive rows at one logical unit
+// must land on 16 distinct (row parity, unit) slots, hence the XOR with
+// (r / 2) % 8 rather than r % 8.
+__device__ __forceinline__ int k2_swz(int row, int unit) { return unit ^ ((row >> 1) & 7); }
 
 template <typename T>
 __device__ __forceinline__ void lds_frag(Frag<T> &f, const unsigned char *row_base, int row, int g) {
@@ -51,13 +65,18 @@ __device__ __forceinline__ void lds_frag(Frag<T> &f, const unsigned char *row_ba
   u32x4 *dst = reinterpret_cast<u32x4 *>(&f);
 #pragma unroll
   for (int u = 0; u < UPF; ++u)
-    dst[u] = *reinterpret_cast<const u32x4 *>(row_base + swz<8>(row, g * UPF + u) * 16);
+    dst[u] = *reinterpret_cast<const u32x4 *>(row_base + k2_swz(row, g * UPF + u) * 16);
+}
+
+__device__ __forceinline__ void wait_vm0() {
+  // s_waitcnt vmcnt(0), other counters unconstrained
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <typename T, int BM, int BN, int BK>
 __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   using C = K2Cfg<T, BM, BN, BK>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -65,60 +84,58 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- block -> (channel, tile row, tile col) --------------------------
-  const int64_t tiles_m = (p.M + BM - 1) / BM;
-  const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t per_ch = tiles_m * tiles_n;
-  const int64_t total = per_ch * kC;
-  const int64_t per_xcd = gridDim.x / kXcds;            // grid is a multiple of kXcds
-  const int64_t logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int per_ch = tiles_m * tiles_n;
+  const int total = per_ch * kC;
+  // Blocks are dispatched in order, round-robin over the XCDs, about
+  // p.slots at a time (one per CU).  Block b of dispatch round s = b / slots
+  // runs on XCD x = (b % slots) % 8; give that XCD the contiguous logical
+  // tiles s*slots + x*(slots/8) + .., so each round works on ~one channel
+  // (its operands stay in the shared last-level cache) and each XCD on a
+  // compact kGroupM x 8 block of it (operand panels shared in its L2).
+  const int slots = p.slots;
+  const int round = blockIdx.x / slots;
+  const int pos = blockIdx.x - round * slots;
+  const int logical = round * slots + (pos % kXcds) * (slots / kXcds) + pos / kXcds;
   if (logical >= total) return;
-  const int64_t d = logical / per_ch;
-  const int64_t t = logical % per_ch;
-  const int64_t group = t / (kGroupM * tiles_n);
-  const int64_t first_m = group * kGroupM;
-  const int64_t gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-  const int64_t tm = first_m + (t % gm);
-  const int64_t tn = (t % (kGroupM * tiles_n)) / gm;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int d = logical / per_ch;
+  const int t = logical - d * per_ch;
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int tm = first_m + (t % gm);
+  const int tn = (t % (kGroupM * tiles_n)) / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
 
-  // ---- staged loads ---------------------------------------------------
-  u32x4 ra[C::A_LD], rb[C::B_LD];
-  auto gload = [&](int ci, int kt) {
+  // ---- direct-to-LDS loads --------------------------------------------
+  // Load instruction i of this wave fills LDS block q = i*4 + wave (1 KB =
+  // 8 rows of 128 bytes); lane l fills row q*8 + l/8, physical unit l%8,
+  // which holds logical unit k2_swz(row, l%8) (the swizzle is an involution).
+  const int lrow = lane >> 3;
+  auto issue_loads = [&](int ci, int kt, int buf) {
     const int64_t ld = p.ch[ci].ld;
-    const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + d * p.M * ld * C::E;
-    const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + d * p.N * ld * C::E;
-    const int64_t kb = (int64_t)kt * BK * C::E;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-      const int u = i * kThreads + tid;
-      const int row = u / C::RU, unit = u % C::RU;
-      int64_t g = m0 + row;
-      g = g < p.M ? g : p.M - 1;
-      ra[i] = *reinterpret_cast<const u32x4 *>(A + g * ld * C::E + kb + unit * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-      const int u = i * kThreads + tid;
-      const int row = u / C::RU, unit = u % C::RU;
-      int64_t g = n0 + row;
-      g = g < p.N ? g : p.N - 1;
-      rb[i] = *reinterpret_cast<const u32x4 *>(B + g * ld * C::E + kb + unit * 16);
-    }
-  };
-  auto lstore = [&](int buf) {
+    const int ldb = (int)(ld * C::E);
+    const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + (int64_t)d * p.M * ld * C::E;
+    const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + (int64_t)d * p.N * ld * C::E;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, (int)(p.M * ldb), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, (int)(p.N * ldb), kRsrcWord3);
+    const int koff = kt * C::ROWB;
     unsigned char *sa = lds + buf * C::STAGE;
     unsigned char *sb = sa + BM * C::ROWB;
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-      const int u = i * kThreads + tid;
-      const int row = u / C::RU, unit = u % C::RU;
-      *reinterpret_cast<u32x4 *>(sa + row * C::ROWB + swz<8>(row, unit) * 16) = ra[i];
+    for (int i = 0; i < C::A_I; ++i) {
+      const int q = i * 4 + wave;
+      const int lunit = k2_swz(q * 8 + lrow, lane & 7);
+      const int row = m0 + q * 8 + lrow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, row * ldb + lunit * 16, koff, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-      const int u = i * kThreads + tid;
-      const int row = u / C::RU, unit = u % C::RU;
-      *reinterpret_cast<u32x4 *>(sb + row * C::ROWB + swz<8>(row, unit) * 16) = rb[i];
+    for (int i = 0; i < C::B_I; ++i) {
+      const int q = i * 4 + wave;
+      const int lunit = k2_swz(q * 8 + lrow, lane & 7);
+      const int row = n0 + q * 8 + lrow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, row * ldb + lunit * 16, koff, 0, 0);
     }
   };
 
@@ -139,58 +156,72 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   };
 
   if (total_kt > 0) {
-    gload(ci, kt);
+    issue_loads(ci, kt, 0);
     advance();
-    lstore(0);
+    wait_vm0();
     __syncthreads();
   }
 
-  for (int it = 0; it < total_kt; ++it) {
-    const int buf = it & 1;
-    const bool has_next = it + 1 < total_kt;
-    if (has_next) gload(ci, kt);
-
+  // One k-tile from LDS stage `buf` on the matrix cores.  The k-fragments of
+  // step ks+1 are read before the matrix-core instructions of step ks are
+  // issued; scheduling barriers keep the compiler from sinking the reads next
+  // to their consumers, so the LDS latency hides behind a whole step of
+  // matrix-core work and one wave per SIMD keeps the matrix core fed.
+  auto compute = [&](int buf, bool with_loads) {
     const unsigned char *sa = lds + buf * C::STAGE;
     const unsigned char *sb = sa + BM * C::ROWB;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
+    Frag<T> af[2][C::MT], bfr[2][C::NT];
+    auto read_frags = [&](int ks, int slot) {
       const int g = 2 * ks + (lane >> 5);  // 8-element group of this lane
-      Frag<T> af[C::MT], bfr[C::NT];
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         const int row = wm * C::WM + mt * 32 + (lane & 31);
-        lds_frag(af[mt], sa + row * C::ROWB, row, g);
+        lds_frag(af[slot][mt], sa + row * C::ROWB, row, g);
       }
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
         const int row = wn * C::WN + nt * 32 + (lane & 31);
-        lds_frag(bfr[nt], sb + row * C::ROWB, row, g);
+        lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, g);
       }
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < C::KS) read_frags(ks + 1, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) mma(acc[mt][nt], af[mt], bfr[nt]);
+        for (int nt = 0; nt < C::NT; ++nt) mma(acc[mt][nt], af[cur][mt], bfr[cur][nt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    (void)with_loads;
+  };
 
-    if (has_next) {
-      lstore(buf ^ 1);
-      advance();
-    }
+  for (int it = 0; it + 1 < total_kt; ++it) {
+    const int buf = it & 1;
+    issue_loads(ci, kt, buf ^ 1);
+    advance();
+    compute(buf, true);
+    wait_vm0();
     __syncthreads();
   }
+  if (total_kt > 0) compute((total_kt - 1) & 1, false);
 
   // ---- write / accumulate x -------------------------------------------
-  float *X = p.x + d * p.M * p.ldx;
+  float *X = p.x + (int64_t)d * p.M * p.ldx;
+  const int M = (int)p.M, N = (int)p.N;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-      const int64_t col = n0 + wn * C::WN + nt * 32 + (lane & 31);
+      const int col = n0 + wn * C::WN + nt * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * C::WM + mt * 32 + acc_row(e, lane);
-        if (row < p.M && col < p.N) {
-          float *dst = X + row * p.ldx + col;
+        const int row = m0 + wm * C::WM + mt * 32 + acc_row(e, lane);
+        if (row < M && col < N) {
+          float *dst = X + (int64_t)row * p.ldx + col;
           *dst = p.accumulate ? *dst + acc[mt][nt][e] : acc[mt][nt][e];
         }
       }
@@ -206,7 +237,10 @@ hipError_t launch_k2(K2Args a, int dtype, hipStream_t s) {
   const int64_t bm = (dtype == TRIMUL_BF16) ? 256 : 128;
   for (int c = 0; c < a.n_chunks; ++c) a.ch[c].ktiles = (int32_t)((a.ch[c].k_len + bk - 1) / bk);
   const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm) * kC;
-  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  // resident work-groups: one per CU for bf16 (128 KB of LDS), two for fp32
+  const int per_cu = (dtype == TRIMUL_BF16) ? 1 : 2;
+  a.slots = (device_cu_count() * per_cu + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = (tiles + a.slots - 1) / a.slots * a.slots;
   if (dtype == TRIMUL_BF16)
     hipLaunchKernelGGL((k2_contract<bf16_t, 256, 256, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else

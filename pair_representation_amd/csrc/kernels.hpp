@@ -43,6 +43,8 @@ struct K2Args {
   K2Chunk ch[TRIMUL_MAX_CHUNKS];
   int32_t n_chunks;
   int32_t accumulate;     // 1: x += result, 0: x = result
+  int32_t slots;          // work-groups resident at once (multiple of 8; set by the launcher)
+  int32_t pad_;
   int64_t M, N;           // tile rows (a operand rows), tile cols (b operand rows)
   float *x;               // [c][M][ldx]
   int64_t ldx;
