@@ -151,12 +151,16 @@ def main():
     ws = pra.new_workspace(w, n, dev)
     out_o = torch.empty((n, n, C_Z), dtype=torch.float32, device=dev)
     out_i = torch.empty_like(out_o)
+    # the workspace of the entry points, viewed as the buffers the kernels use:
+    # a and b operands (operand layout), then the contraction result
     kp = (n + 63) // 64 * 64
-    elt = 2 if work.dtype == "bf16" else 4
-    plane = (C * n * kp * elt + 255) // 256 * 256
-    a_pl = ws[:C * n * kp * elt].view(torch.bfloat16 if elt == 2 else torch.float32).view(C, n, kp)
-    b_pl = ws[plane:plane + C * n * kp * elt].view(a_pl.dtype).view(C, n, kp)
-    x = ws[2 * plane:2 * plane + C * n * n * 4].view(torch.float32).view(C, n, n)
+    td = w.torch_dtype
+    op_bytes = pra.tile_operand_bytes(w, n, kp)
+    plane = (op_bytes + 255) // 256 * 256
+    xbytes = pra.tile_xacc_bytes(w, n, n)
+    a_pl = ws[:op_bytes].view(td).view(pra.operand_shape(n, kp))
+    b_pl = ws[plane:plane + op_bytes].view(td).view(pra.operand_shape(n, kp))
+    x = ws[2 * plane:2 * plane + xbytes].view(torch.float32).view(pra.xacc_shape(n, n))
     torch.cuda.synchronize()
 
     def step_api():

@@ -98,14 +98,20 @@ typedef struct {
 } trimul_weights_t;
 
 /* One k-chunk of the contraction for a tile: the operands of residues
- * k_off .. k_off+k_len-1.
- *   a: [c][n_rows][ld]  a[d][r][t] = operand of (row_off + r, k_off + t)
- *   b: [c][n_cols][ld]  b[d][s][t] = operand of (col_off + s, k_off + t)
+ * k_off .. k_off+k_len-1, as two operand buffers
+ *   a[d][r][t] = operand of (row_off + r, k_off + t),  r < n_rows, t < ld
+ *   b[d][s][t] = operand of (col_off + s, k_off + t),  s < n_cols, t < ld
  * where "operand of (i, k)" is a_ik, b_jk for outgoing and a_ki, b_kj for
  * incoming (incoming operands are stored transposed so one layout serves
  * both).  Element type = the weights' dtype.  ld is a multiple of 64,
  * ld >= k_len, and columns k_len .. ld-1 must hold zeros (trimul_tile_operands
- * writes them). */
+ * writes them).
+ *
+ * Operand layout: blocks of 256 rows x 64 columns; element [d][r][t] sits at
+ *   ((r/256 * ld/64 + t/64) * 128 + d) * 16384 + (r%256) * 64 + t%64
+ * i.e. the 128 channel blocks of one (row block, column block) are adjacent
+ * and rows are padded to a multiple of 256 (padding rows are never read into
+ * a stored result; trimul_tile_operand_bytes gives the size). */
 typedef struct {
   int64_t k_off;
   int64_t k_len;
@@ -115,9 +121,10 @@ typedef struct {
 } trimul_kchunk_t;
 
 /* Bytes of workspace trimul_outgoing / trimul_incoming need for size n: the
- * a and b operand planes [c][n][round_up(n, 64)] (element = dtype) and the fp32
- * contraction result [c][n][n], each rounded up to 256 bytes.  Returns 0 for
- * an invalid w or n. */
+ * a and b operands of all n rows with ld = round_up(n, 64) in the operand
+ * layout of trimul_kchunk_t (element = dtype), and the fp32 contraction result
+ * in the x_acc layout of trimul_tile for an n x n tile, each rounded up to 256
+ * bytes.  Returns 0 for an invalid w or n. */
 size_t trimul_workspace_bytes(const trimul_weights_t *w, int64_t n);
 
 /* The full update over an n x n pair grid, outgoing direction.
@@ -135,7 +142,8 @@ trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const 
                                 float *out, int64_t n, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
-/* Bytes of one operand buffer of trimul_tile_operands: c * rows * ld * elt. */
+/* Bytes of one operand buffer of trimul_tile_operands:
+ * c * round_up(rows, 256) * ld * elt. */
 size_t trimul_tile_operand_bytes(const trimul_weights_t *w, int64_t rows, int64_t ld);
 
 /* The operand chunk a device owning z contributes for one tile: runs the
@@ -152,11 +160,23 @@ trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir
                                      int64_t k_off, int64_t k_len, int64_t ld, void *a_out,
                                      void *b_out, void *stream);
 
+/* Bytes of the fp32 tile accumulator x_acc of trimul_tile:
+ * c * round_up(n_rows, 4) * round_up(n_cols, 16) * 4. */
+size_t trimul_tile_xacc_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols);
+
 /* One device's tile of the pair grid: rows row_off .. row_off+n_rows-1, cols
  * col_off .. col_off+n_cols-1.  Contracts the given chunks (host array, in
- * arrival order) into
- *   x_acc[d][r][s]  (fp32, [c][n_rows][n_cols])
- * overwriting it when flags has TRIMUL_TILE_FIRST and adding to it otherwise;
+ * arrival order) into the fp32 accumulator x_acc, stored in blocks of 4 rows
+ * x 16 columns with the 128 channels of a block adjacent, so that the
+ * contraction writes 16-byte groups and the epilogue reads one contiguous
+ * 32 KB block per 64 pairs:
+ *   x_(row_off+r, col_off+s), channel d, sits at element
+ *   ((r/4 * ldx/16 + s/16) * 128 + d) * 64 + (s%16) * 4 + r%4,
+ *   ldx = round_up(n_cols, 16), r < round_up(n_rows, 4)
+ * (trimul_tile_xacc_bytes bytes; entries of rows past n_rows or columns past
+ * n_cols are unspecified and never read into a result), overwriting it when
+ * flags has
+ * TRIMUL_TILE_FIRST and adding to it otherwise;
  * the partial sums stay in registers across the chunks of one call.  With
  * TRIMUL_TILE_LAST the epilogue then writes
  *   out_tile[r][s][e] (fp32, [n_rows][n_cols][c_z])

@@ -79,6 +79,8 @@ def lib():
             f.restype = ctypes.c_int
         L.trimul_tile_operand_bytes.argtypes = [W, i64, i64]
         L.trimul_tile_operand_bytes.restype = sz
+        L.trimul_tile_xacc_bytes.argtypes = [W, i64, i64]
+        L.trimul_tile_xacc_bytes.restype = sz
         L.trimul_tile_operands.argtypes = [W, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                            i64, vp, vp, vp]
         L.trimul_tile_operands.restype = ctypes.c_int
@@ -194,40 +196,89 @@ def incoming(z, mask, w: Weights, workspace=None, out=None):
     return _full(lib().trimul_incoming, z, mask, w, workspace, out)
 
 
+def operand_shape(rows, ld):
+    """Shape of one operand buffer in the library's operand layout: blocks of
+    256 rows x 64 columns, the 128 channel blocks of a block adjacent:
+    [ceil(rows/256), ld/64, 128, 256, 64]."""
+    return ((rows + 255) // 256, ld // 64, C, 256, 64)
+
+
+def new_operand(rows, ld, dtype, device="cuda"):
+    return torch.empty(operand_shape(rows, ld), dtype=dtype, device=device)
+
+
+def operand_to_planar(op, rows):
+    """[128, rows, ld] copy of an operand buffer (layout conversion only)."""
+    rb, kb = op.shape[0], op.shape[1]
+    return op.permute(2, 0, 3, 1, 4).reshape(C, rb * 256, kb * 64)[:, :rows]
+
+
+def planar_to_operand(planar):
+    """Operand buffer holding planar [128, rows, ld] (rows zero-padded to 256)."""
+    _, rows, ld = planar.shape
+    rb = (rows + 255) // 256
+    full = torch.zeros((C, rb * 256, ld), dtype=planar.dtype, device=planar.device)
+    full[:, :rows] = planar
+    return full.reshape(C, rb, 256, ld // 64, 64).permute(1, 3, 0, 2, 4).contiguous()
+
+
 def tile_operands(w: Weights, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld,
                   a_out=None, b_out=None, want_a=True, want_b=True):
-    """Operand chunk [128, rows, ld] for one tile and k-range; returns (a, b)."""
+    """Operand chunk (operand layout, see operand_shape) for one tile and
+    k-range; returns (a, b)."""
     n = z.shape[0]
     _need(z, "z", w.torch_dtype, (n, n, C_Z))
     _need(mask, "mask", torch.uint8, (n, n))
     if want_a and a_out is None:
-        a_out = torch.empty((C, n_rows, ld), dtype=w.torch_dtype, device=z.device)
+        a_out = new_operand(n_rows, ld, w.torch_dtype, z.device)
     if want_b and b_out is None:
-        b_out = torch.empty((C, n_cols, ld), dtype=w.torch_dtype, device=z.device)
+        b_out = new_operand(n_cols, ld, w.torch_dtype, z.device)
     if a_out is not None:
-        _need(a_out, "a_out", w.torch_dtype, (C, n_rows, ld))
+        _need(a_out, "a_out", w.torch_dtype, operand_shape(n_rows, ld))
     if b_out is not None:
-        _need(b_out, "b_out", w.torch_dtype, (C, n_cols, ld))
+        _need(b_out, "b_out", w.torch_dtype, operand_shape(n_cols, ld))
     _check(lib().trimul_tile_operands(w.ref, direction, _ptr(z), _ptr(mask), n, row_off, n_rows, col_off,
                                       n_cols, k_off, k_len, ld, _ptr(a_out), _ptr(b_out), _stream()))
     return a_out, b_out
 
 
+def tile_xacc_bytes(w: Weights, n_rows: int, n_cols: int) -> int:
+    return int(lib().trimul_tile_xacc_bytes(w.ref, n_rows, n_cols))
+
+
+def xacc_shape(n_rows, n_cols):
+    """Shape of a tile accumulator: blocks of 4 rows x 16 columns, the 128
+    channels of a block adjacent: [ceil(n_rows/4), ceil(n_cols/16), 128, 16, 4]."""
+    return ((n_rows + 3) // 4, (n_cols + 15) // 16, C, 16, 4)
+
+
+def new_xacc(n_rows, n_cols, device="cuda"):
+    """Tile accumulator (uninitialised fp32, see xacc_shape)."""
+    return torch.empty(xacc_shape(n_rows, n_cols), dtype=torch.float32, device=device)
+
+
+def xacc_to_planar(x_acc, n_rows, n_cols):
+    """[128, n_rows, n_cols] copy of an accumulator (layout conversion only)."""
+    rb, cb = x_acc.shape[0], x_acc.shape[1]
+    return x_acc.permute(2, 0, 4, 1, 3).reshape(C, rb * 4, cb * 16)[:, :n_rows, :n_cols]
+
+
 def tile(w: Weights, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z=None, mask=None,
          out_tile=None):
     """Contract ``chunks`` (list of (k_off, k_len, a, b) in arrival order) into
-    x_acc [128, n_rows, n_cols]; with TILE_LAST also write out_tile
+    x_acc (see new_xacc for its layout); with TILE_LAST also write out_tile
     [n_rows, n_cols, 128] fp32 (allocated if None).  Returns out_tile."""
-    _need(x_acc, "x_acc", torch.float32, (C, n_rows, n_cols))
+    _need(x_acc, "x_acc", torch.float32, xacc_shape(n_rows, n_cols))
     arr = (KChunk * max(1, len(chunks)))()
     for i, (k_off, k_len, a, b) in enumerate(chunks):
         _need(a, f"chunk {i} a", w.torch_dtype)
         _need(b, f"chunk {i} b", w.torch_dtype)
-        if a.dim() != 3 or a.shape[0] != C or a.shape[1] != n_rows:
-            raise ValueError(f"chunk {i} a must be [128, {n_rows}, ld]")
-        if b.dim() != 3 or b.shape[0] != C or b.shape[1] != n_cols or b.shape[2] != a.shape[2]:
-            raise ValueError(f"chunk {i} b must be [128, {n_cols}, ld] with a's ld")
-        arr[i] = KChunk(k_off, k_len, a.shape[2], a.data_ptr(), b.data_ptr())
+        ld = a.shape[1] * 64 if a.dim() == 5 else -1
+        if tuple(a.shape) != operand_shape(n_rows, ld):
+            raise ValueError(f"chunk {i} a must have shape operand_shape({n_rows}, ld)")
+        if tuple(b.shape) != operand_shape(n_cols, ld):
+            raise ValueError(f"chunk {i} b must have shape operand_shape({n_cols}, ld) with a's ld")
+        arr[i] = KChunk(k_off, k_len, ld, a.data_ptr(), b.data_ptr())
     if flags & TILE_LAST:
         _need(z, "z", w.torch_dtype, (n, n, C_Z))
         _need(mask, "mask", torch.uint8, (n, n))

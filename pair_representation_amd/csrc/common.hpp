@@ -103,6 +103,33 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
+// Layout of the contraction operands in HBM.  A logical operand plane set
+// a[d][r][t] (channel d < 128, row r, column t < ld, ld a multiple of 64) is
+// stored in blocks of kOpRows rows x kOpCols columns; the 128 channel blocks
+// of one (row block, column block) are adjacent, each kOpRows * kOpCols
+// elements, rows of a block contiguous.  The projection kernel writes one row
+// of all 128 channels of a block per work item (a few pages), and the
+// contraction kernel reads a whole 256 x 64 operand tile of one channel as one
+// contiguous run.  Rows are padded to a multiple of kOpRows.
+constexpr int kOpRows = 256;
+constexpr int kOpCols = 64;
+constexpr int64_t kOpBlock = (int64_t)kOpRows * kOpCols;   // elements per channel block
+
+__device__ __forceinline__ int64_t operand_offset(int64_t r, int64_t t, int d, int64_t ld) {
+  return (((r / kOpRows) * (ld / kOpCols) + t / kOpCols) * kC + d) * kOpBlock + (r % kOpRows) * kOpCols +
+         (t % kOpCols);
+}
+
+// Layout of the contraction result x[d][i][j] of a tile in HBM: blocks of
+// 4 rows x 16 columns with all 128 channels of a block adjacent, channel-major
+// inside, element (ii, jj) of a block at 4*jj + ii.  One epilogue work item
+// (4 rows x 16 columns) reads one contiguous 32 KB block; the contraction
+// kernel writes 16-byte groups (4 rows of one column).  ldx = columns padded
+// to a multiple of 16; rows padded to a multiple of 4.
+__device__ __forceinline__ int64_t x_offset(int64_t i, int64_t j, int d, int64_t ldx) {
+  return (((i >> 2) * (ldx >> 4) + (j >> 4)) * kC + d) * 64 + (j & 15) * 4 + (i & 3);
+}
+
 // XOR swizzle of 16-byte units inside an LDS row: unit u of row `row` is
 // stored at unit u ^ (row % period).  Applied on both write and read, it
 // spreads the 32 rows a k-fragment read touches over distinct banks.

@@ -1,21 +1,25 @@
 // K1: input LayerNorm, the four c_z -> c projections, sigmoid gates and the
 // pair mask, producing the contraction operands
 //     a = m * sigmoid(W_a_gate zh) * (W_a_proj zh),  b likewise,
-// as channel-planar, k-contiguous planes  plane[d][r][t]  (one 64-pair run of
-// t per work item).  For the incoming direction the source pair of (r, t) is
-// (t, r), so the planes come out transposed and the contraction kernel is the
-// same for both directions.
+// as channel-planar, k-contiguous planes  plane[d][r][t].  For the incoming
+// direction the source pair of plane cell (r, t) is (t, r), so the planes come
+// out transposed and the contraction kernel is the same for both directions.
 //
 // Work item: 64 consecutive plane columns t of one plane row r (64 pairs).
-// 256 threads: every thread loads four 8-channel units of z (16 lanes per
-// pair), the LayerNorm statistics are 16-lane shuffle reductions, and the
-// normalised pairs go to LDS (bf16 when the weights are bf16) as the matrix-
-// core B operand.  Wave w owns operand w/2 (a or b) and channels
-// 64*(w%2) .. +63: projection rows and gate rows of the same channels land in
-// the same lanes, so the gate product is formed in registers.  The kernel is
-// persistent (one pass over the work items with stride gridDim.x); bf16 weight
-// fragments stay in registers for the whole pass and the next item's z is
-// prefetched while the current one is on the matrix cores.
+// 512 threads = 8 waves, two per SIMD, persistent over the work items with
+// stride gridDim.x.
+//  - z of the next item is prefetched into registers while the current one is
+//    processed: every thread holds two 8-channel units (16 lanes per pair).
+//  - LayerNorm statistics are 16-lane shuffle reductions; the normalised pairs
+//    go to LDS (rounded to bf16 when the weights are bf16) with an XOR
+//    swizzle, together with the 64 pair-mask bytes.
+//  - Matrix-core product with pairs as rows: out[pair][col] = zh . W[col].
+//    Wave w owns operand w/4 (a or b) and channels 32*(w%4) .. +31: its
+//    32 projection columns and the 32 gate columns of the same channels land
+//    in the same lanes, so the gated product is formed in registers.  bf16
+//    weight fragments stay in registers for the whole pass.
+//  - Each lane ends up with 4 consecutive pairs of one channel, stored as one
+//    8-byte (bf16) or 16-byte (fp32) write.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,7 +28,7 @@ namespace trimul {
 namespace {
 
 constexpr int kPairs = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 template <typename T>
 struct ZUnit;  // 8 channels of one pair as loaded from HBM
@@ -69,8 +73,14 @@ __device__ __forceinline__ void put_unit(unsigned char *dst, const float (&f)[8]
   reinterpret_cast<f32x4 *>(dst)[1] = f32x4{f[4], f[5], f[6], f[7]};
 }
 
-__device__ __forceinline__ void store_elem(bf16_t *p, float v) { p->v = f32_to_bf16(v); }
-__device__ __forceinline__ void store_elem(float *p, float v) { *p = v; }
+// Four consecutive plane elements of one channel.
+__device__ __forceinline__ void store4(bf16_t *p, const float (&v)[4]) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float *p, const float (&v)[4]) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
@@ -79,10 +89,11 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   constexpr int ROWB = kCz * E;        // bytes of one pair row in LDS
   constexpr bool kWeightsInRegs = (E == 2);
   __shared__ __attribute__((aligned(16))) unsigned char zh_lds[kPairs * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t mask_lds[kPairs];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int64_t tiles_per_row = p.ld / kPairs;
   const int64_t n_tiles = p.n_rows * tiles_per_row;
 
@@ -92,31 +103,30 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) { g8[i] = p.ln_w[cg * 8 + i]; b8[i] = p.ln_b[cg * 8 + i]; }
 
-  // this wave's operand and weight rows
-  const int op = wave >> 1;        // 0: a, 1: b
-  const int c0 = 64 * (wave & 1);  // first channel
+  // this wave's operand and weight columns
+  const int op = wave >> 2;        // 0: a, 1: b
+  const int c0 = 32 * (wave & 3);  // first channel
   T *const out_plane = static_cast<T *>(op == 0 ? p.a_out : p.b_out);
   const T *const Wp = static_cast<const T *>(op == 0 ? p.w_a_proj : p.w_b_proj);
   const T *const Wg = static_cast<const T *>(op == 0 ? p.w_a_gate : p.w_b_gate);
   const bool active = out_plane != nullptr;   // wave-uniform
 
-  // m-tile mt: 0,1 -> projection rows c0+32*mt ; 2,3 -> gate rows c0+32*(mt-2)
-  auto wfrag_ptr = [&](int mt, int ks) -> const T * {
-    const T *W = (mt < 2) ? Wp : Wg;
-    const int row = c0 + 32 * (mt & 1) + (lane & 31);
-    return W + row * kCz + 16 * ks + 8 * (lane >> 5);
+  // column tile nt: 0 -> projection rows c0..c0+31, 1 -> gate rows c0..c0+31
+  auto wfrag_ptr = [&](int nt, int ks) -> const T * {
+    const T *W = (nt == 0) ? Wp : Wg;
+    return W + (c0 + (lane & 31)) * kCz + 16 * ks + 8 * (lane >> 5);
   };
-  Frag<T> wreg[kWeightsInRegs ? 4 : 1][kWeightsInRegs ? 8 : 1];
+  Frag<T> wreg[kWeightsInRegs ? 2 : 1][kWeightsInRegs ? 8 : 1];
   if constexpr (kWeightsInRegs) {
     if (active) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) wreg[mt][ks].load(wfrag_ptr(mt, ks));
+        for (int ks = 0; ks < 8; ++ks) wreg[nt][ks].load(wfrag_ptr(nt, ks));
     }
   }
 
-  // source pair of plane cell (r, t); returns false past k_len
+  // source pair of plane cell (r, t); false past k_len
   auto src_pair = [&](int64_t r, int64_t t, int64_t &i, int64_t &j) -> bool {
     if (t >= p.k_len) return false;
     if (p.transposed) { i = p.k_off + t; j = p.row_base + r; }
@@ -125,31 +135,43 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   };
 
   const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
-  ZUnit<T> raw[4];
+  ZUnit<T> raw[2];
+  uint8_t mraw = 0;
   auto load_tile = [&](int64_t tile) {
     const int64_t r = tile / tiles_per_row;
     const int64_t t0 = (tile % tiles_per_row) * kPairs;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int q = 16 * s + (tid >> 4);   // pair within the tile
+    for (int s = 0; s < 2; ++s) {
+      const int q = 32 * s + (tid >> 4);   // pair within the tile
       int64_t i, j;
       if (src_pair(r, t0 + q, i, j))
         raw[s].load(zbytes + ((i * p.n + j) * kCz + cg * 8) * E);
       else
         raw[s].zero();
     }
+    if (tid < kPairs) {
+      int64_t i, j;
+      mraw = src_pair(r, t0 + tid, i, j) ? (p.mask[i * p.n + j] != 0) : 0;
+    }
   };
 
-  int64_t tile = blockIdx.x;
-  if (tile < n_tiles) load_tile(tile);
+  // Each work-group takes a contiguous range of work items: consecutive items
+  // continue along the same plane row, so the 256 channel planes it writes
+  // stay in the same few pages (scattering items over the grid makes nearly
+  // every store miss the address-translation cache).
+  const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
+  const int64_t tile_begin = blockIdx.x * per_wg;
+  const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
+  int64_t tile = tile_begin;
+  if (tile < tile_end) load_tile(tile);
 
-  for (; tile < n_tiles; tile += gridDim.x) {
+  for (; tile < tile_end; ++tile) {
     const int64_t r = tile / tiles_per_row;
     const int64_t t0 = (tile % tiles_per_row) * kPairs;
 
     // ---- LayerNorm of the 64 pairs -> LDS --------------------------------
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       float f[8];
       raw[s].to_f32(f);
       float sum = 0.f;
@@ -162,19 +184,20 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       const float rstd = rsqrt_f32(group_sum<16>(sq) * (1.0f / kCz) + p.eps);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * rstd * g8[i] + b8[i];
-      const int q = 16 * s + (tid >> 4);
+      const int q = 32 * s + (tid >> 4);
       put_unit(zh_lds + q * ROWB + swz<16>(q, cg) * UNIT, f, T{});
     }
+    if (tid < kPairs) mask_lds[tid] = mraw;
     __syncthreads();
 
     // ---- prefetch the next work item ------------------------------------
-    if (tile + gridDim.x < n_tiles) load_tile(tile + gridDim.x);
+    if (tile + 1 < tile_end) load_tile(tile + 1);
 
     // ---- projections on the matrix cores --------------------------------
     if (active) {
-      f32x16 acc[4][2];
+      f32x16 acc[2][2];   // [pair tile][proj, gate]
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -182,38 +205,42 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
 
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        Frag<T> bf[2];
+        Frag<T> zf[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int q = 32 * nt + (lane & 31);
+        for (int mt = 0; mt < 2; ++mt) {
+          const int q = 32 * mt + (lane & 31);
           const int unit = 2 * ks + (lane >> 5);
-          bf[nt].load(zh_lds + q * ROWB + swz<16>(q, unit) * UNIT);
+          zf[mt].load(zh_lds + q * ROWB + swz<16>(q, unit) * UNIT);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          Frag<T> af;
-          if constexpr (kWeightsInRegs) af = wreg[mt][ks];
-          else af.load(wfrag_ptr(mt, ks));
+        for (int nt = 0; nt < 2; ++nt) {
+          Frag<T> wf;
+          if constexpr (kWeightsInRegs) wf = wreg[nt][ks];
+          else wf.load(wfrag_ptr(nt, ks));
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], af, bf[nt]);
+          for (int mt = 0; mt < 2; ++mt) mma(acc[mt][nt], zf[mt], wf);
         }
       }
 
-      // ---- gate, mask, store ---------------------------------------------
+      // ---- gate, mask, store: 4 consecutive pairs of channel d per lane ---
+      const int d = c0 + (lane & 31);
+      // operand layout: blocks of 256 rows x 64 columns, all channels of a
+      // block adjacent (see operand_offset); this item is one row of block
+      // (r / 256, t0 / 64), 128 contiguous bytes per channel
+      T *const prow = out_plane + operand_offset(r, t0, d, p.ld);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int q = 32 * nt + (lane & 31);
-        const int64_t t = t0 + q;
-        int64_t i, j;
-        bool keep = src_pair(r, t, i, j) && p.mask[i * p.n + j] != 0;
+      for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int g = 0; g < 4; ++g) {
+          const int q0 = 32 * mt + acc_row(4 * g, lane);
+          const uint32_t m4 = *reinterpret_cast<const uint32_t *>(mask_lds + q0);
+          float v[4];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int d = c0 + 32 * mt + acc_row(e, lane);
-            const float v = keep ? sigmoid_f32(acc[mt + 2][nt][e]) * acc[mt][nt][e] : 0.f;
-            store_elem(out_plane + ((int64_t)d * p.n_rows + r) * p.ld + t, v);
+          for (int i = 0; i < 4; ++i) {
+            const bool keep = (m4 >> (8 * i)) & 0xff;
+            v[i] = keep ? sigmoid_f32(acc[mt][1][4 * g + i]) * acc[mt][0][4 * g + i] : 0.f;
           }
+          store4(prow + q0, v);
         }
       }
     }
@@ -226,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
 hipError_t launch_k1(const K1Args &a, int dtype, hipStream_t s) {
   const int64_t n_tiles = a.n_rows * (a.ld / kPairs);
   if (n_tiles <= 0) return hipSuccess;
-  // one resident work-group per CU (register-limited), persistent over items
+  // one resident work-group per CU, persistent over the work items
   const int64_t grid = n_tiles < device_cu_count() ? n_tiles : device_cu_count();
   if (dtype == TRIMUL_BF16)
     hipLaunchKernelGGL(k1_project<bf16_t>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);

@@ -15,9 +15,12 @@
 // fills 1 KB of LDS (64 lanes x 16 bytes at consecutive addresses), so the
 // XOR swizzle of 16-byte units inside a row (unit u of row r stored at
 // u ^ ((r / 2) % 8)) is applied on the global side: a lane fetches the
-// logical unit that belongs in its LDS slot.  Rows past the end of the operand fall outside
-// the buffer's range and read as zeros.  k-fragments are read from LDS one
-// 16-wide k step ahead of the matrix-core instructions that consume them.
+// logical unit that belongs in its LDS slot.  In the operand layout (see
+// operand_offset) a k-tile of one channel is a single contiguous 32 KB run;
+// rows past the operand's end are padding rows of the last 256-row block and
+// only feed output rows/columns that are never stored.  k-fragments are read
+// from LDS one 16-wide k step ahead of the matrix-core instructions that
+// consume them.
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
@@ -114,28 +117,35 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // which holds logical unit k2_swz(row, l%8) (the swizzle is an involution).
   const int lrow = lane >> 3;
   auto issue_loads = [&](int ci, int kt, int buf) {
+    // The k-tile is one contiguous run of one channel block of each operand
+    // (256 rows x 64 columns per block; a BK-wide k-tile is columns kk ..
+    // kk+BK-1 of it, rows m0 % 256 ..).
     const int64_t ld = p.ch[ci].ld;
-    const int ldb = (int)(ld * C::E);
-    const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + (int64_t)d * p.M * ld * C::E;
-    const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + (int64_t)d * p.N * ld * C::E;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, (int)(p.M * ldb), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, (int)(p.N * ldb), kRsrcWord3);
-    const int koff = kt * C::ROWB;
+    const int64_t kcol = (int64_t)kt * BK;
+    const int64_t cb = kcol / kOpCols;
+    const int kk = (int)(kcol % kOpCols);
+    const int64_t a_blk = ((int64_t)(m0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
+    const int64_t b_blk = ((int64_t)(n0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
+    const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + a_blk * kOpBlock * C::E;
+    const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + b_blk * kOpBlock * C::E;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
+    const int a_row0 = m0 % kOpRows, b_row0 = n0 % kOpRows;
     unsigned char *sa = lds + buf * C::STAGE;
     unsigned char *sb = sa + BM * C::ROWB;
 #pragma unroll
     for (int i = 0; i < C::A_I; ++i) {
       const int q = i * 4 + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
-      const int row = m0 + q * 8 + lrow;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, row * ldb + lunit * 16, koff, 0, 0);
+      const int off = ((a_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
       const int q = i * 4 + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
-      const int row = n0 + q * 8 + lrow;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, row * ldb + lunit * 16, koff, 0, 0);
+      const int off = ((b_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -210,19 +220,25 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   if (total_kt > 0) compute((total_kt - 1) & 1, false);
 
   // ---- write / accumulate x -------------------------------------------
-  float *X = p.x + (int64_t)d * p.M * p.ldx;
-  const int M = (int)p.M, N = (int)p.N;
+  // The four accumulator registers 4g..4g+3 of a lane are rows 4k..4k+3 of
+  // one column: one 16-byte group of the x layout (x_offset); 16 lanes cover
+  // the 16 columns of a 256-byte block row.  Rows of the last 4-row group
+  // past M hold products of padding rows and are ignored downstream.
+  const int M4 = (int)((p.M + 3) & ~int64_t(3));
+  const int N = (int)p.N;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const int col = n0 + wn * C::WN + nt * 32 + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * C::WM + mt * 32 + acc_row(e, lane);
-        if (row < M && col < N) {
-          float *dst = X + (int64_t)row * p.ldx + col;
-          *dst = p.accumulate ? *dst + acc[mt][nt][e] : acc[mt][nt][e];
+      for (int g = 0; g < 4; ++g) {
+        const int row4 = m0 + wm * C::WM + mt * 32 + acc_row(4 * g, lane);   // multiple of 4
+        if (row4 < M4 && col < N) {
+          f32x4 *dst = reinterpret_cast<f32x4 *>(p.x + x_offset(row4, col, d, p.ldx));
+          f32x4 v = {acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1], acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]};
+          if (p.accumulate) v += *dst;
+          *dst = v;
         }
       }
     }

@@ -1,21 +1,26 @@
 // K3: the epilogue of the update for a tile of the pair grid,
 //     out_ij = m_ij * sigmoid(W_out_gate LN_in(z_ij)) * (W_out_proj LN_out(x_ij))
-// reading the channel-planar contraction result x[d][r][s] and the pair
-// tensor, writing fp32 out[r][s][e].
+// reading the contraction result x (blocks of 4 rows x 16 columns x 128
+// channels, see x_offset) and the
+// pair tensor, writing fp32 out[r][s][e].
 //
-// Work item: 64 consecutive columns s of one tile row r (64 pairs), 256
-// threads.  x is read channel by channel (64 lanes = 256 contiguous bytes per
-// channel), each wave holding 32 channels of all 64 pairs; the output
-// LayerNorm statistics are combined across the four waves through LDS.  z is
-// re-read (16 lanes per pair, 16-lane shuffle reductions) and re-normalised
-// for the gate.  Both normalised operands go to LDS as matrix-core B
-// operands; in bf16 mode each is split into hi + lo bf16 terms (hi = bf16(v),
-// lo = bf16(v - hi)) and multiplied by the bf16 weights twice, so the
-// products keep fp32-level accuracy.  Wave w computes output channels
-// 32w .. 32w+31 of both the projection and the gate, so the final product is
-// formed in registers, staged through LDS and stored as whole 512-byte pair
-// rows.  Persistent over the work items; bf16 weight fragments stay in
-// registers.
+// Work item: 64 pairs = 4 consecutive rows x 16 consecutive columns, pair
+// index p = 4*jj + ii, which is also the order of one channel's 64 values in
+// x (256 contiguous bytes).  512 threads = 8 waves (two per SIMD), persistent
+// over the work items; the next item's x and z are prefetched into registers
+// while the current one is processed.
+//  - x: thread (pair p = tid % 64, channel group tid / 64) holds 16 channels;
+//    output LayerNorm statistics are combined over the 8 groups in LDS.
+//  - z is re-read (16 lanes per pair, 16-lane shuffle reductions) and
+//    re-normalised for the gate.
+//  - Both normalised operands go to LDS as matrix-core B operands; in bf16
+//    mode each is split into hi + lo bf16 terms (hi = bf16(v),
+//    lo = bf16(v - hi)) and multiplied by the bf16 weights twice, so the
+//    products keep fp32-level accuracy.
+//  - Wave w computes output channels 32*(w%4) .. +31 of both the projection
+//    and the gate for pairs 32*(w/4) .. +31, so the final product is formed in
+//    registers; it is staged through LDS and stored as whole 512-byte pair
+//    rows.  bf16 weight fragments stay in registers for the whole pass.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,8 +29,10 @@ namespace trimul {
 namespace {
 
 constexpr int kPairs = 64;
-constexpr int kThreads = 256;
-constexpr int kOutRowF = kCz + 4;  // staged output row (floats), padded against bank conflicts
+constexpr int kRows = 4, kCols = 16;  // work-item shape
+constexpr int kThreads = 512;
+constexpr int kOutRowF = kCz + 4;     // staged output row (floats), padded against bank conflicts
+constexpr int kXPer = kC / 8;         // x channels per thread
 
 template <typename T>
 struct ZUnit;
@@ -117,30 +124,39 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   constexpr int kStageBytes = kPairs * kOutRowF * 4;
   constexpr int kLdsBytes = (2 * kOpBytes) > kStageBytes ? (2 * kOpBytes) : kStageBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float red[4][kPairs];
+  __shared__ float red[8][kPairs];
   __shared__ float stat_mean[kPairs], stat_rstd[kPairs];
+  __shared__ __attribute__((aligned(4))) uint8_t mask_lds[kPairs];
   unsigned char *const n_ops = lds;               // normalised x
   unsigned char *const z_ops = lds + kOpBytes;    // normalised z
   float *const stage = reinterpret_cast<float *>(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t tiles_per_row = (p.n_cols + kPairs - 1) / kPairs;
-  const int64_t n_tiles = p.n_rows * tiles_per_row;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int64_t rows4 = (p.n_rows + 3) / 4;
+  const int64_t tiles_per_blk = (p.n_cols + kCols - 1) / kCols;
+  const int64_t n_tiles = rows4 * tiles_per_blk;
 
-  // LayerNorm parameters: x channels 32*wave .. +31 for this thread; z channel
-  // group (tid & 15) for the gate path
+  // x channels of this thread: xc0 .. xc0+15 of pair q = lane
+  const int q = lane;
+  const int xc0 = kXPer * wave;
+  float gx[kXPer], bx[kXPer];
+#pragma unroll
+  for (int c = 0; c < kXPer; ++c) { gx[c] = p.ln_out_w[xc0 + c]; bx[c] = p.ln_out_b[xc0 + c]; }
+  // z units of this thread: pairs 32*s + tid/16, channel group tid & 15
   const int cg = tid & 15;
   float gz[8], bz[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { gz[i] = p.ln_in_w[cg * 8 + i]; bz[i] = p.ln_in_b[cg * 8 + i]; }
 
+  // matrix-core rows (output channels) and pair half of this wave
+  const int o0 = 32 * (wave & 3);
+  const int ph = 32 * (wave >> 2);
   const T *const Wo = static_cast<const T *>(p.w_out_proj);
   const T *const Wg = static_cast<const T *>(p.w_out_gate);
   auto wptr = [&](const T *W, int ks) -> const T * {
-    const int row = 32 * wave + (lane & 31);
-    return W + row * kC + 16 * ks + 8 * (lane >> 5);
+    return W + (o0 + (lane & 31)) * kC + 16 * ks + 8 * (lane >> 5);
   };
   Frag<T> wo[kWeightsInRegs ? 8 : 1], wg[kWeightsInRegs ? 8 : 1];
   if constexpr (kWeightsInRegs) {
@@ -150,62 +166,85 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
 
   const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
 
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t r = tile / tiles_per_row;
-    const int64_t s0 = (tile % tiles_per_row) * kPairs;
-    const int64_t gi = p.row_off + r;                 // global row of the tile row
-
-    // ---- x: this thread holds pair q = lane, channels 32*wave .. +31 ------
-    const int q = lane;
-    const bool qv = s0 + q < p.n_cols;
-    float xv[32];
-    const float *xp = p.x + (int64_t)(32 * wave) * p.n_rows * p.ldx + r * p.ldx + s0 + q;
+  // ---- per-item loads (prefetched one item ahead) --------------------------
+  float xv[kXPer];
+  ZUnit<T> zr[2];
+  uint8_t mraw = 0;
+  auto load_item = [&](int64_t tile) {
+    const int64_t blk = tile / tiles_per_blk;
+    const int64_t s0 = (tile % tiles_per_blk) * kCols;
+    // x: the item is one 4 x 16 block of the x layout (x_offset): 128
+    // channels x 64 pairs, contiguous, pair q at 4*jj + ii of each channel
+    const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) xv[c] = qv ? xp[(int64_t)c * p.n_rows * p.ldx] : 0.f;
-
-    // ---- z units for the gate: pairs 16s + tid/16, channels cg*8 .. +7 -----
-    ZUnit<T> zr[4];
+    for (int c = 0; c < kXPer; ++c) xv[c] = xp[c * 64];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int qq = 16 * s + (tid >> 4);
-      if (s0 + qq < p.n_cols)
-        zr[s].load(zbytes + ((gi * p.n + p.col_off + s0 + qq) * kCz + cg * 8) * E);
+    for (int s = 0; s < 2; ++s) {
+      const int qq = 32 * s + (tid >> 4);
+      const int64_t r = blk * 4 + (qq & 3), col = s0 + (qq >> 2);
+      if (r < p.n_rows && col < p.n_cols)
+        zr[s].load(zbytes + (((p.row_off + r) * p.n + p.col_off + col) * kCz + cg * 8) * E);
       else
         zr[s].zero();
     }
+    if (tid < kPairs) {
+      const int64_t r = blk * 4 + (tid & 3), col = s0 + (tid >> 2);
+      mraw = (r < p.n_rows && col < p.n_cols) ? (p.mask[(p.row_off + r) * p.n + p.col_off + col] != 0) : 0;
+    }
+  };
 
-    // ---- output LayerNorm statistics (two passes, across the 4 waves) -----
+  // Each work-group takes a contiguous range of work items, so consecutive
+  // items read neighbouring columns of every x channel plane and of z (few
+  // pages in the address-translation cache at a time).
+  const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
+  const int64_t tile_begin = blockIdx.x * per_wg;
+  const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
+  int64_t tile = tile_begin;
+  if (tile < tile_end) load_item(tile);
+
+  for (; tile < tile_end; ++tile) {
+    const int64_t blk = tile / tiles_per_blk;
+    const int64_t s0 = (tile % tiles_per_blk) * kCols;
+
+    // ---- output LayerNorm statistics (two passes, across the 8 groups) ----
     float sum = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) sum += xv[c];
+    for (int c = 0; c < kXPer; ++c) sum += xv[c];
     red[wave][q] = sum;
+    if (tid < kPairs) mask_lds[tid] = mraw;
     __syncthreads();
-    if (tid < kPairs) stat_mean[tid] = (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) * (1.0f / kC);
+    if (tid < kPairs) {
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) t += red[g][tid];
+      stat_mean[tid] = t * (1.0f / kC);
+    }
     __syncthreads();
     const float mean = stat_mean[q];
     float sq = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) { xv[c] -= mean; sq += xv[c] * xv[c]; }
+    for (int c = 0; c < kXPer; ++c) { xv[c] -= mean; sq += xv[c] * xv[c]; }
     red[wave][q] = sq;
     __syncthreads();
-    if (tid < kPairs)
-      stat_rstd[tid] = rsqrt_f32((red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) * (1.0f / kC) + p.eps);
+    if (tid < kPairs) {
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) t += red[g][tid];
+      stat_rstd[tid] = rsqrt_f32(t * (1.0f / kC) + p.eps);
+    }
     __syncthreads();
     const float rstd = stat_rstd[q];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kXPer / 8; ++u) {
       float f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = 32 * wave + 8 * u + i;
-        f[i] = xv[8 * u + i] * rstd * p.ln_out_w[c] + p.ln_out_b[c];
-      }
-      Op::put(n_ops, q, 4 * wave + u, f);
+      for (int i = 0; i < 8; ++i) f[i] = xv[8 * u + i] * rstd * gx[8 * u + i] + bx[8 * u + i];
+      Op::put(n_ops, q, xc0 / 8 + u, f);
     }
 
     // ---- input LayerNorm of z (recomputed) for the gate --------------------
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       float f[8];
       zr[s].to_f32(f);
       float zs = 0.f;
@@ -215,63 +254,56 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       float zq = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { f[i] -= zm; zq += f[i] * f[i]; }
-      const float zr_std = rsqrt_f32(group_sum<16>(zq) * (1.0f / kCz) + p.eps);
+      const float zrs = rsqrt_f32(group_sum<16>(zq) * (1.0f / kCz) + p.eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = f[i] * zr_std * gz[i] + bz[i];
-      Op::put(z_ops, 16 * s + (tid >> 4), cg, f);
+      for (int i = 0; i < 8; ++i) f[i] = f[i] * zrs * gz[i] + bz[i];
+      Op::put(z_ops, 32 * s + (tid >> 4), cg, f);
     }
     __syncthreads();
 
+    // ---- prefetch the next item ----------------------------------------------
+    if (tile + 1 < tile_end) load_item(tile + 1);
+
     // ---- projections on the matrix cores ----------------------------------
-    f32x16 ay[2], ag[2];
+    f32x16 ay, ag;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { ay[nt][e] = 0.f; ag[nt][e] = 0.f; }
+    for (int e = 0; e < 16; ++e) { ay[e] = 0.f; ag[e] = 0.f; }
+    const int pq = ph + (lane & 31);   // this lane's pair column
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       Frag<T> fo, fg;
       if constexpr (kWeightsInRegs) { fo = wo[ks]; fg = wg[ks]; }
       else { fo.load(wptr(Wo, ks)); fg.load(wptr(Wg, ks)); }
       const int unit = 2 * ks + (lane >> 5);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int qq = 32 * nt + (lane & 31);
-        Op::mma_at(ay[nt], fo, n_ops, qq, unit);
-        Op::mma_at(ag[nt], fg, z_ops, qq, unit);
-      }
+      Op::mma_at(ay, fo, n_ops, pq, unit);
+      Op::mma_at(ag, fg, z_ops, pq, unit);
     }
+    const bool keep = mask_lds[pq] != 0;
     __syncthreads();   // operands consumed; LDS becomes the output stage
 
     // ---- gate * projection * mask -> LDS stage -----------------------------
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int qq = 32 * nt + (lane & 31);
-      const bool keep = (s0 + qq < p.n_cols) && p.mask[gi * p.n + p.col_off + s0 + qq] != 0;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 v;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g4 + i;
-          v[i] = keep ? sigmoid_f32(ag[nt][e]) * ay[nt][e] : 0.f;
-        }
-        const int o = 32 * wave + acc_row(4 * g4, lane);
-        *reinterpret_cast<f32x4 *>(stage + qq * kOutRowF + o) = v;
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g4 + i;
+        v[i] = keep ? sigmoid_f32(ag[e]) * ay[e] : 0.f;
       }
+      const int o = o0 + acc_row(4 * g4, lane);
+      *reinterpret_cast<f32x4 *>(stage + pq * kOutRowF + o) = v;
     }
     __syncthreads();
 
     // ---- stage -> HBM: whole pair rows, 16 bytes per lane ------------------
-    const int64_t nq = (p.n_cols - s0) < kPairs ? (p.n_cols - s0) : kPairs;
-    float *orow = p.out + (r * p.n_cols + s0) * kCz;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int u = i * kThreads + tid;
-      const int qq = u >> 5, o4 = (u & 31) * 4;
-      if (qq < nq)
-        *reinterpret_cast<f32x4 *>(orow + qq * kCz + o4) =
-            *reinterpret_cast<const f32x4 *>(stage + qq * kOutRowF + o4);
+      const int pp = u >> 5, o4 = (u & 31) * 4;
+      const int64_t r = blk * 4 + (pp & 3), col = s0 + (pp >> 2);
+      if (r < p.n_rows && col < p.n_cols)
+        *reinterpret_cast<f32x4 *>(p.out + (r * p.n_cols + col) * kCz + o4) =
+            *reinterpret_cast<const f32x4 *>(stage + pp * kOutRowF + o4);
     }
     __syncthreads();
   }
@@ -280,9 +312,9 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
 }  // namespace
 
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s) {
-  const int64_t n_tiles = a.n_rows * ((a.n_cols + kPairs - 1) / kPairs);
+  const int64_t n_tiles = ((a.n_rows + 3) / 4) * ((a.n_cols + kCols - 1) / kCols);
   if (n_tiles <= 0) return hipSuccess;
-  const int64_t cap = 2LL * device_cu_count();
+  const int64_t cap = device_cu_count();
   const int64_t grid = n_tiles < cap ? n_tiles : cap;
   if (dtype == TRIMUL_BF16)
     hipLaunchKernelGGL(k3_epilogue<bf16_t>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);

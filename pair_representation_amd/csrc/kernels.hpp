@@ -46,12 +46,12 @@ struct K2Args {
   int32_t slots;          // work-groups resident at once (multiple of 8; set by the launcher)
   int32_t pad_;
   int64_t M, N;           // tile rows (a operand rows), tile cols (b operand rows)
-  float *x;               // [c][M][ldx]
+  float *x;               // [c][round_up(M,4)/4][ldx][4] (4-row blocks), ldx = round_up(N,16)
   int64_t ldx;
 };
 
 struct K3Args {
-  const float *x;         // [c][n_rows][ldx] contraction result of the tile
+  const float *x;         // [c][round_up(n_rows,4)/4][ldx][4] contraction result of the tile
   int64_t ldx;
   const void *z;          // [n][n][c_z] global
   const uint8_t *mask;    // [n][n] global

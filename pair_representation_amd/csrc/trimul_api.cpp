@@ -59,6 +59,20 @@ trimul_status_t check_weights(const trimul_weights_t *w) {
   return TRIMUL_OK;
 }
 
+// Contraction result of a rows x cols tile: x[d][r/4][s][r%4], rows padded to
+// a multiple of 4 and columns to a multiple of 16.
+int64_t x_ld(int64_t cols) { return round_up(cols, 16); }
+size_t xacc_bytes(int64_t rows, int64_t cols) {
+  return (size_t)128 * round_up(rows, 4) * x_ld(cols) * sizeof(float);
+}
+
+// Operand chunk of `rows` rows and row length ld in the blocked operand layout
+// (blocks of 256 rows x 64 columns, 128 channel blocks adjacent): rows are
+// padded to a multiple of 256.
+size_t operand_bytes(int64_t rows, int64_t ld, int32_t dtype) {
+  return (size_t)128 * round_up(rows, 256) * ld * elt_bytes(dtype);
+}
+
 struct FullLayout {
   int64_t kp;       // padded k extent = row length of the operand planes
   size_t a_off, b_off, x_off, total;
@@ -67,11 +81,11 @@ struct FullLayout {
 FullLayout full_layout(int32_t dtype, int64_t n) {
   FullLayout L;
   L.kp = round_up(n, kKTile);
-  const size_t plane = align256((size_t)128 * n * L.kp * elt_bytes(dtype));
+  const size_t plane = align256(operand_bytes(n, L.kp, dtype));
   L.a_off = 0;
   L.b_off = plane;
   L.x_off = 2 * plane;
-  L.total = L.x_off + align256((size_t)128 * n * n * sizeof(float));
+  L.total = L.x_off + align256(xacc_bytes(n, n));
   return L;
 }
 
@@ -161,11 +175,11 @@ trimul_status_t run_full(const trimul_weights_t *w, const void *z, const uint8_t
   k2.M = n;
   k2.N = n;
   k2.x = x;
-  k2.ldx = n;
+  k2.ldx = x_ld(n);
   e = trimul::launch_k2(k2, w->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "contraction kernel launch");
 
-  trimul::K3Args k3 = k3_args(w, x, n, z, mask, n, 0, n, 0, n, out);
+  trimul::K3Args k3 = k3_args(w, x, x_ld(n), z, mask, n, 0, n, 0, n, out);
   e = trimul::launch_k3(k3, w->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
   return ok();
@@ -211,9 +225,14 @@ trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const 
   return run_full(w, z, mask, out, n, workspace, workspace_bytes, stream, true);
 }
 
+size_t trimul_tile_xacc_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols) {
+  if (!w || n_rows < 0 || n_cols < 0) return 0;
+  return xacc_bytes(n_rows, n_cols);
+}
+
 size_t trimul_tile_operand_bytes(const trimul_weights_t *w, int64_t rows, int64_t ld) {
   if (!w || (w->dtype != TRIMUL_F32 && w->dtype != TRIMUL_BF16) || rows < 0 || ld < 0) return 0;
-  return (size_t)128 * rows * ld * elt_bytes(w->dtype);
+  return operand_bytes(rows, ld, w->dtype);
 }
 
 trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
@@ -337,12 +356,12 @@ trimul_status_t trimul_tile(const trimul_weights_t *w, int64_t n, int64_t row_of
     k2.M = n_rows;
     k2.N = n_cols;
     k2.x = x_acc;
-    k2.ldx = n_cols;
+    k2.ldx = x_ld(n_cols);
     e = trimul::launch_k2(k2, w->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "contraction kernel launch");
   }
   if (last) {
-    trimul::K3Args k3 = k3_args(w, x_acc, n_cols, z, mask, n, row_off, n_rows, col_off, n_cols, out_tile);
+    trimul::K3Args k3 = k3_args(w, x_acc, x_ld(n_cols), z, mask, n, row_off, n_rows, col_off, n_cols, out_tile);
     e = trimul::launch_k3(k3, w->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
   }

@@ -67,8 +67,10 @@ def test_workspace_closed_form(dtype, elt, n):
     w = weights(dtype)
     kp = round_up(n, 64)
     a256 = lambda v: round_up(v, 256)
-    want = 2 * a256(128 * n * kp * elt) + a256(128 * n * n * 4)
+    xacc = 128 * round_up(n, 4) * round_up(n, 16) * 4
+    want = 2 * a256(128 * round_up(n, 256) * kp * elt) + a256(xacc)
     assert pra.lib().trimul_workspace_bytes(ctypes.byref(w), n) == want
+    assert pra.lib().trimul_tile_xacc_bytes(ctypes.byref(w), n, n) == xacc
 
 
 def test_workspace_invalid():
@@ -77,7 +79,8 @@ def test_workspace_invalid():
     assert L.trimul_workspace_bytes(ctypes.byref(weights()), -1) == 0
     assert L.trimul_workspace_bytes(ctypes.byref(weights()), 70000) == 0
     assert L.trimul_workspace_bytes(ctypes.byref(weights(dtype=7)), 10) == 0
-    assert L.trimul_tile_operand_bytes(ctypes.byref(weights()), 5000, 1280) == 128 * 5000 * 1280 * 2
+    # operand rows are padded to a multiple of 256
+    assert L.trimul_tile_operand_bytes(ctypes.byref(weights()), 5000, 1280) == 128 * 5120 * 1280 * 2
 
 
 def test_n_zero_is_noop():

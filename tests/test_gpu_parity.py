@@ -141,8 +141,8 @@ def test_operand_planes(dev, dtype, direction):
     d = pra.OUTGOING if direction == "outgoing" else pra.INCOMING
     a, b = pra.tile_operands(w, d, z, mask, 0, n, 0, n, 0, n, ld)
     torch.cuda.synchronize()
-    a = a.double().cpu().numpy()
-    b = b.double().cpu().numpy()
+    a = pra.operand_to_planar(a, n).double().cpu().numpy()
+    b = pra.operand_to_planar(b, n).double().cpu().numpy()
     qa, qb = oracle.project(h["z"], h["mask"], h["w"], quant=(dtype == "bf16"))
     if direction == "incoming":
         qa, qb, m = np.swapaxes(qa, 0, 1), np.swapaxes(qb, 0, 1), h["mask"].T
@@ -192,12 +192,14 @@ def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     B[:, :, :klen] = torch.from_numpy(b).to(td)
     _, _, wts = wl.make_small(4, seed=1, dtype=dtype, device="cpu")
     w = pra.Weights(wts, pra.BF16 if dtype == "bf16" else pra.F32, device=dev)
-    x = torch.full((128, m_rows, n_cols), float("nan"), device=dev)
+    x = pra.new_xacc(m_rows, n_cols, dev).fill_(float("nan"))
     n = max(m_rows, n_cols, klen)
-    pra.tile(w, n, 0, m_rows, 0, n_cols, [(0, klen, A.to(dev), B.to(dev))], pra.TILE_FIRST, x)
+    Ab = pra.planar_to_operand(A.to(dev))
+    Bb = pra.planar_to_operand(B.to(dev))
+    pra.tile(w, n, 0, m_rows, 0, n_cols, [(0, klen, Ab, Bb)], pra.TILE_FIRST, x)
     torch.cuda.synchronize()
     ref = np.einsum("dik,djk->dij", a, b)
-    e = rel_err(x.cpu().double().numpy(), ref)
+    e = rel_err(pra.xacc_to_planar(x, m_rows, n_cols).cpu().double().numpy(), ref)
     print(f"  contraction {dtype} {m_rows}x{n_cols}x{klen}: {e:.3e}")
     assert e <= 1e-5
 
@@ -229,7 +231,7 @@ def test_tile_matches_oracle(dev, dtype, direction):
     # ring order for this tile: start at the block holding its own rows
     start = [i for i, c in enumerate(chunks) if c[0] <= row_off < c[0] + c[1]][0]
     ring = chunks[start:] + chunks[:start]
-    x = torch.empty((128, n_rows, n_cols), device=dev)
+    x = pra.new_xacc(n_rows, n_cols, dev)
     out = pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring, pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
     torch.cuda.synchronize()
 
@@ -245,7 +247,8 @@ def test_tile_matches_oracle(dev, dtype, direction):
     # x of the tile: oracle partial sums per chunk add up to the GPU's x
     xs = sum(oracle.tile_partial(gz, gm, n, h["w"], direction, rows, cols, np.arange(k, k + kl), quant)
              for k, kl, _, _ in ring)
-    assert rel_err(np.moveaxis(x.cpu().double().numpy(), 0, 2), xs) <= tol
+    xpl = pra.xacc_to_planar(x, n_rows, n_cols)
+    assert rel_err(np.moveaxis(xpl.cpu().double().numpy(), 0, 2), xs) <= tol
 
     # rotated order in one call
     rot = ring[3:] + ring[:3]
@@ -257,8 +260,8 @@ def test_tile_matches_oracle(dev, dtype, direction):
     pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring[1:3], 0, x3)
     out3 = pra.tile(w, n, row_off, n_rows, col_off, n_cols, ring[3:], pra.TILE_LAST, x3, z, mask)
     torch.cuda.synchronize()
-    assert rel_err(x2.cpu().numpy(), x.cpu().numpy()) <= 1e-5
-    assert rel_err(x3.cpu().numpy(), x.cpu().numpy()) <= 1e-5
+    for xo in (x2, x3):
+        assert rel_err(pra.xacc_to_planar(xo, n_rows, n_cols).cpu().numpy(), xpl.cpu().numpy()) <= 1e-5
     assert rel_err(out2.cpu().numpy(), out.cpu().numpy()) <= 1e-4
     assert rel_err(out3.cpu().numpy(), out.cpu().numpy()) <= 1e-4
     # epilogue alone on a finished x_acc (no chunks, LAST)
@@ -282,7 +285,7 @@ def test_tiles_assemble_full_grid(dev):
                 a, b = pra.tile_operands(w, pra.OUTGOING, z, mask, ro, h2, co, h2, k_off, k_len, 128)
                 chunks.append((k_off, k_len, a, b))
             order = chunks[p:] + chunks[:p]
-            x = torch.empty((128, h2, h2), device=dev)
+            x = pra.new_xacc(h2, h2, dev)
             asm[ro:ro + h2, co:co + h2] = pra.tile(w, n, ro, h2, co, h2, order,
                                                    pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
     torch.cuda.synchronize()

@@ -148,7 +148,7 @@ def test_n10000_tile_sampled(dev, direction):
         a, b = pra.tile_operands(w, d, z, mask, t["row_off"], t["n_rows"], t["col_off"], t["n_cols"],
                                  k_off, t["chunk"], ld)
         chunks.append((k_off, t["chunk"], a, b))
-    x = torch.empty((128, t["n_rows"], t["n_cols"]), device=dev)
+    x = pra.new_xacc(t["n_rows"], t["n_cols"], dev)
     out = pra.tile(w, work.n, t["row_off"], t["n_rows"], t["col_off"], t["n_cols"], chunks,
                    pra.TILE_FIRST | pra.TILE_LAST, x, z, mask)
     torch.cuda.synchronize()
