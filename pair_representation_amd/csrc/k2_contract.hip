@@ -4,8 +4,10 @@
 // x_ij = sum_k a_ki * b_kj  for the transposed incoming operands.  Per channel
 // d this is one "NT" matrix product (both operands k-contiguous).
 //
-// Work-group tile BM x BN of one channel, four waves in a 2 x 2 layout, each
-// wave a (BM/2) x (BN/2) block of 32 x 32 matrix-core accumulators.  The
+// Work-group tile BM x BN of one channel, eight waves (two per SIMD) in a
+// 2 x 4 layout, each wave a (BM/2) x (BN/4) block of 32 x 32 matrix-core
+// accumulators; the two waves of a SIMD hide each other's LDS and barrier
+// latency.  The
 // k-loop walks the chunks in the order given (a ring's delivery order) and,
 // inside each chunk, BK-wide k-tiles.
 //
@@ -33,7 +35,7 @@ namespace trimul {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
@@ -45,7 +47,7 @@ struct K2Cfg {
   static constexpr int E = sizeof(T);
   static constexpr int ROWB = BK * E;          // bytes per LDS row
   static constexpr int RU = ROWB / 16;         // 16-byte units per row
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WM = BM / 2, WN = BN / 4;
   static constexpr int MT = WM / 32, NT = WN / 32;
   static constexpr int KS = BK / 16;           // 16-wide k steps per k-tile
   static constexpr int A_I = BM * RU / kThreads;    // 1 KB load instructions per wave (A)
@@ -83,8 +85,10 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  // wave-uniform (scalar): the per-instruction load descriptors derived from
+  // it must live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
 
   // ---- block -> (channel, tile row, tile col) --------------------------
   const int tiles_m = (int)((p.M + BM - 1) / BM);
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   const int m0 = tm * BM, n0 = tn * BN;
 
   // ---- direct-to-LDS loads --------------------------------------------
-  // Load instruction i of this wave fills LDS block q = i*4 + wave (1 KB =
+  // Load instruction i of this wave fills LDS block q = i*8 + wave (1 KB =
   // 8 rows of 128 bytes); lane l fills row q*8 + l/8, physical unit l%8,
   // which holds logical unit k2_swz(row, l%8) (the swizzle is an involution).
   const int lrow = lane >> 3;
@@ -124,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
     const int64_t kcol = (int64_t)kt * BK;
     const int64_t cb = kcol / kOpCols;
     const int kk = (int)(kcol % kOpCols);
+    // tiles never straddle a 256-row block (BM, BN divide 256)
     const int64_t a_blk = ((int64_t)(m0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
     const int64_t b_blk = ((int64_t)(n0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
     const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + a_blk * kOpBlock * C::E;
@@ -135,14 +140,14 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
     unsigned char *sb = sa + BM * C::ROWB;
 #pragma unroll
     for (int i = 0; i < C::A_I; ++i) {
-      const int q = i * 4 + wave;
+      const int q = i * 8 + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((a_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
-      const int q = i * 4 + wave;
+      const int q = i * 8 + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((b_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, off, 0, 0, 0);
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // step ks+1 are read before the matrix-core instructions of step ks are
   // issued; scheduling barriers keep the compiler from sinking the reads next
   // to their consumers, so the LDS latency hides behind a whole step of
-  // matrix-core work and one wave per SIMD keeps the matrix core fed.
+  // matrix-core work and the matrix core stays fed.
   auto compute = [&](int buf, bool with_loads) {
     const unsigned char *sa = lds + buf * C::STAGE;
     const unsigned char *sb = sa + BM * C::ROWB;
@@ -250,9 +255,10 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   const int64_t bk = (dtype == TRIMUL_BF16) ? 64 : 32;
-  const int64_t bm = (dtype == TRIMUL_BF16) ? 256 : 128;
+  const int64_t bn = (dtype == TRIMUL_BF16) ? 256 : 128;
+  const int64_t bm = bn;
   for (int c = 0; c < a.n_chunks; ++c) a.ch[c].ktiles = (int32_t)((a.ch[c].k_len + bk - 1) / bk);
-  const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm) * kC;
+  const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * kC;
   // resident work-groups: one per CU for bf16 (128 KB of LDS), two for fp32
   const int per_cu = (dtype == TRIMUL_BF16) ? 1 : 2;
   a.slots = (device_cu_count() * per_cu + kXcds - 1) / kXcds * kXcds;
