@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n3605_4ch")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="row block for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
