@@ -32,8 +32,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two values rounded to bf16 (round to nearest even) in one packed word, lo in
+// the low half: a single packed conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Logistic function 1 / (1 + e^-t) from the identity e^u = 2^(u log2 e) on
@@ -53,6 +57,22 @@ template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over each row of 16 lanes with DPP lane permutations (no LDS traffic):
+// swap neighbours, swap neighbouring pairs, mirror inside each half-row of 8,
+// mirror inside the row.  Every step adds two equal partial sums in either
+// order, so all 16 lanes receive bit-identical totals.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
   return v;
 }
 

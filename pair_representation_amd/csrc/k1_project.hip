@@ -1,25 +1,27 @@
 // K1: input LayerNorm, the four c_z -> c projections, sigmoid gates and the
 // pair mask, producing the contraction operands
 //     a = m * sigmoid(W_a_gate zh) * (W_a_proj zh),  b likewise,
-// as channel-planar, k-contiguous planes  plane[d][r][t].  For the incoming
-// direction the source pair of plane cell (r, t) is (t, r), so the planes come
-// out transposed and the contraction kernel is the same for both directions.
+// in the blocked operand layout (see operand_offset).  For the incoming
+// direction the source pair of plane cell (r, t) is (t, r), so the operands
+// come out transposed and the contraction kernel is the same for both
+// directions.
 //
 // Work item: 64 consecutive plane columns t of one plane row r (64 pairs).
-// 512 threads = 8 waves, two per SIMD, persistent over the work items with
-// stride gridDim.x.
-//  - z of the next item is prefetched into registers while the current one is
-//    processed: every thread holds two 8-channel units (16 lanes per pair).
-//  - LayerNorm statistics are 16-lane shuffle reductions; the normalised pairs
-//    go to LDS (rounded to bf16 when the weights are bf16) with an XOR
-//    swizzle, together with the 64 pair-mask bytes.
-//  - Matrix-core product with pairs as rows: out[pair][col] = zh . W[col].
+// 512 threads = 8 waves, two per SIMD; each work-group walks a contiguous
+// range of items, software-pipelined over three items:
+//  - z of item i+2 is loaded into registers (16 lanes per pair, two 8-channel
+//    units per thread) while item i is processed;
+//  - the LayerNorm of item i+1 (16-lane DPP reductions, result rounded to the
+//    weight type) is written to the other half of a double-buffered LDS tile,
+//    its instructions interleaved with the matrix-core products of item i;
+//  - matrix-core product with pairs as rows: out[pair][col] = zh . W[col].
 //    Wave w owns operand w/4 (a or b) and channels 32*(w%4) .. +31: its
 //    32 projection columns and the 32 gate columns of the same channels land
-//    in the same lanes, so the gated product is formed in registers.  bf16
-//    weight fragments stay in registers for the whole pass.
-//  - Each lane ends up with 4 consecutive pairs of one channel, stored as one
-//    8-byte (bf16) or 16-byte (fp32) write.
+//    in the same lanes, so the gated, masked product is formed in registers
+//    (bf16 weight fragments stay in registers for the whole pass);
+//  - one barrier per item.
+// Each lane ends up with 4 consecutive pairs of one channel, stored as one
+// 8-byte (bf16) or 16-byte (fp32) write.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -87,9 +89,11 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   constexpr int E = sizeof(T);
   constexpr int UNIT = 8 * E;          // bytes of one 8-channel unit
   constexpr int ROWB = kCz * E;        // bytes of one pair row in LDS
+  constexpr int OUTB = kPairs * E;     // bytes of one channel's output row of an item
+  constexpr int OSTR = OUTB + 4 * E;   // padded staging stride (conflict-free writes)
   constexpr bool kWeightsInRegs = (E == 2);
-  __shared__ __attribute__((aligned(16))) unsigned char zh_lds[kPairs * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t mask_lds[kPairs];
+  __shared__ __attribute__((aligned(16))) unsigned char zh_lds[2][kPairs * ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char out_lds[kThreads / 64][32 * OSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,58 +122,62 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   };
   Frag<T> wreg[kWeightsInRegs ? 2 : 1][kWeightsInRegs ? 8 : 1];
   if constexpr (kWeightsInRegs) {
-    if (active) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) wreg[nt][ks].load(wfrag_ptr(nt, ks));
-    }
+      for (int ks = 0; ks < 8; ++ks) wreg[nt][ks].load(wfrag_ptr(nt, ks));
   }
 
-  // source pair of plane cell (r, t); false past k_len
-  auto src_pair = [&](int64_t r, int64_t t, int64_t &i, int64_t &j) -> bool {
-    if (t >= p.k_len) return false;
-    if (p.transposed) { i = p.k_off + t; j = p.row_base + r; }
-    else { i = p.row_base + r; j = p.k_off + t; }
-    return true;
-  };
-
-  const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
-  ZUnit<T> raw[2];
-  uint8_t mraw = 0;
-  auto load_tile = [&](int64_t tile) {
-    const int64_t r = tile / tiles_per_row;
-    const int64_t t0 = (tile % tiles_per_row) * kPairs;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int q = 32 * s + (tid >> 4);   // pair within the tile
-      int64_t i, j;
-      if (src_pair(r, t0 + q, i, j))
-        raw[s].load(zbytes + ((i * p.n + j) * kCz + cg * 8) * E);
-      else
-        raw[s].zero();
-    }
-    if (tid < kPairs) {
-      int64_t i, j;
-      mraw = src_pair(r, t0 + tid, i, j) ? (p.mask[i * p.n + j] != 0) : 0;
-    }
-  };
-
   // Each work-group takes a contiguous range of work items: consecutive items
-  // continue along the same plane row, so the 256 channel planes it writes
-  // stay in the same few pages (scattering items over the grid makes nearly
-  // every store miss the address-translation cache).
+  // continue along the same plane row, so the channel blocks it writes stay in
+  // the same few pages (scattering items over the grid makes nearly every
+  // store miss the address-translation cache).
   const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
   const int64_t tile_begin = blockIdx.x * per_wg;
   const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
-  int64_t tile = tile_begin;
-  if (tile < tile_end) load_tile(tile);
+  if (tile_begin >= tile_end) return;
 
-  for (; tile < tile_end; ++tile) {
-    const int64_t r = tile / tiles_per_row;
-    const int64_t t0 = (tile % tiles_per_row) * kPairs;
+  // plane position (row r, first column t0) of a work item, advanced in order
+  struct Pos {
+    int64_t r, t0;
+  };
+  auto pos_of = [&](int64_t tile) { return Pos{tile / tiles_per_row, (tile % tiles_per_row) * kPairs}; };
+  auto next_pos = [&](Pos q) {
+    q.t0 += kPairs;
+    if (q.t0 == p.ld) { q.t0 = 0; ++q.r; }
+    return q;
+  };
 
-    // ---- LayerNorm of the 64 pairs -> LDS --------------------------------
+  // Loads of z and mask for a work item.  Cells past k_len (and rows past the
+  // last item, which the pipeline touches after the end of its range) read a
+  // valid stand-in pair and count as masked, so the code stays branch-free.
+  const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
+  ZUnit<T> raw[2];
+  bool keep[2];
+  auto pair_index = [&](int64_t r, int64_t t, bool &valid) -> int64_t {
+    valid = t < p.k_len && r < p.n_rows;
+    const int64_t rr = r < p.n_rows ? r : p.n_rows - 1;
+    const int64_t tt = t < p.k_len ? t : 0;
+    const int64_t i = p.transposed ? p.k_off + tt : p.row_base + rr;
+    const int64_t j = p.transposed ? p.row_base + rr : p.k_off + tt;
+    return i * p.n + j;
+  };
+  auto load_item = [&](Pos q) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int pr = 32 * s + (tid >> 4);   // pair within the item
+      bool valid;
+      const int64_t idx = pair_index(q.r, q.t0 + pr, valid);
+      raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
+      const uint8_t mb = p.mask[idx];
+      keep[s] = valid && mb != 0;
+    }
+  };
+
+  // LayerNorm of the item held in `raw` -> LDS buffer `buf`.  A masked pair's
+  // row is stored as zeros: its projections are then exactly 0 and so is the
+  // gated product sigmoid(0) * 0, which applies the pair mask to a and b.
+  auto layer_norm = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float f[8];
@@ -177,73 +185,96 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) sum += f[i];
-      const float mean = group_sum<16>(sum) * (1.0f / kCz);
+      const float mean = row_sum16(sum) * (1.0f / kCz);
       float sq = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { f[i] -= mean; sq += f[i] * f[i]; }
-      const float rstd = rsqrt_f32(group_sum<16>(sq) * (1.0f / kCz) + p.eps);
+      const float rstd = rsqrt_f32(row_sum16(sq) * (1.0f / kCz) + p.eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = f[i] * rstd * g8[i] + b8[i];
-      const int q = 32 * s + (tid >> 4);
-      put_unit(zh_lds + q * ROWB + swz<16>(q, cg) * UNIT, f, T{});
+      for (int i = 0; i < 8; ++i) f[i] = keep[s] ? f[i] * rstd * g8[i] + b8[i] : 0.f;
+      const int pr = 32 * s + (tid >> 4);
+      put_unit(zh_lds[buf] + pr * ROWB + swz<16>(pr, cg) * UNIT, f, T{});
     }
-    if (tid < kPairs) mask_lds[tid] = mraw;
-    __syncthreads();
+  };
 
-    // ---- prefetch the next work item ------------------------------------
-    if (tile + 1 < tile_end) load_tile(tile + 1);
-
-    // ---- projections on the matrix cores --------------------------------
-    if (active) {
-      f32x16 acc[2][2];   // [pair tile][proj, gate]
+  f32x16 acc[2][2];   // [pair tile][proj, gate]
+  // products of pair tile mt (pairs 32mt .. 32mt+31) with this wave's 32
+  // projection and 32 gate columns
+  auto products = [&](int buf, int mt) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.f;
-
+    for (int ks = 0; ks < 8; ++ks) {
+      Frag<T> zf;
+      const int q = 32 * mt + (lane & 31);
+      zf.load(zh_lds[buf] + q * ROWB + swz<16>(q, 2 * ks + (lane >> 5)) * UNIT);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        Frag<T> zf[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int q = 32 * mt + (lane & 31);
-          const int unit = 2 * ks + (lane >> 5);
-          zf[mt].load(zh_lds + q * ROWB + swz<16>(q, unit) * UNIT);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          Frag<T> wf;
-          if constexpr (kWeightsInRegs) wf = wreg[nt][ks];
-          else wf.load(wfrag_ptr(nt, ks));
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) mma(acc[mt][nt], zf[mt], wf);
-        }
-      }
-
-      // ---- gate, mask, store: 4 consecutive pairs of channel d per lane ---
-      const int d = c0 + (lane & 31);
-      // operand layout: blocks of 256 rows x 64 columns, all channels of a
-      // block adjacent (see operand_offset); this item is one row of block
-      // (r / 256, t0 / 64), 128 contiguous bytes per channel
-      T *const prow = out_plane + operand_offset(r, t0, d, p.ld);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q0 = 32 * mt + acc_row(4 * g, lane);
-          const uint32_t m4 = *reinterpret_cast<const uint32_t *>(mask_lds + q0);
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool keep = (m4 >> (8 * i)) & 0xff;
-            v[i] = keep ? sigmoid_f32(acc[mt][1][4 * g + i]) * acc[mt][0][4 * g + i] : 0.f;
-          }
-          store4(prow + q0, v);
-        }
+      for (int nt = 0; nt < 2; ++nt) {
+        Frag<T> wf;
+        if constexpr (kWeightsInRegs) wf = wreg[nt][ks];
+        else wf.load(wfrag_ptr(nt, ks));
+        mma(acc[mt][nt], zf, wf);
       }
     }
+  };
+  // gated products of pair tile mt -> this wave's staging rows (row = channel
+  // c0 + lane % 32; each lane holds 4 consecutive pairs per register group)
+  unsigned char *const stage = out_lds[wave];
+  auto gate = [&](int mt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sigmoid_f32(acc[mt][1][4 * g + i]) * acc[mt][0][4 * g + i];
+      const int q0 = 32 * mt + acc_row(4 * g, lane);
+      store4(reinterpret_cast<T *>(stage + (lane & 31) * OSTR) + q0, v);
+    }
+  };
+  // staging rows -> HBM: one 16-byte piece per lane, whole 128-byte (bf16)
+  // or 256-byte (fp32) channel rows per group of lanes.  The operand layout
+  // keeps the 64 columns of an item contiguous within each channel block.
+  auto store_out = [&](Pos q) {
+    constexpr int LPR = OUTB / 16;     // lanes per channel row
+    constexpr int RPI = 64 / LPR;      // rows per instruction
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / LPR;
+      const int piece = lane % LPR;
+      const u32x2 *src = reinterpret_cast<const u32x2 *>(stage + row * OSTR + piece * 16);
+      const u32x2 lo = src[0], hi = src[1];
+      if (active)
+        *reinterpret_cast<u32x4 *>(out_plane + operand_offset(q.r, q.t0, c0 + row, p.ld) + piece * (16 / E)) =
+            u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+
+  // prologue: item 0 normalised into buffer 0, item 1 in registers
+  Pos cur = pos_of(tile_begin);
+  load_item(cur);
+  layer_norm(0);
+  Pos ahead = next_pos(cur);       // the item held in `raw`
+  load_item(ahead);
+  __syncthreads();
+
+  // One barrier per item.  The matrix-core products of this item, the
+  // LayerNorm of the next one, the loads of the one after and the gates of
+  // pair tile 0 are mutually independent straight-line code, so the compiler
+  // interleaves vector work with the matrix-core instructions.  Waves with no
+  // output run the products on unused weights and skip the stores.
+  for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
+    const int buf = (int)((tile - tile_begin) & 1);
+    products(buf, 0);
+    layer_norm(buf ^ 1);   // after the last item: a stand-in nobody reads
+    products(buf, 1);
+    gate(0);
+    ahead = next_pos(ahead);
+    load_item(ahead);
+    gate(1);
+    store_out(cur);
+    cur = next_pos(cur);
     __syncthreads();
   }
 }
