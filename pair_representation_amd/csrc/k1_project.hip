@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kPairs = 64;
 constexpr int kThreads = 512;
+constexpr int kRowGroup = 16;   // plane rows walked per column block
 
 template <typename T>
 struct ZUnit;  // 8 channels of one pair as loaded from HBM
@@ -128,23 +129,40 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       for (int ks = 0; ks < 8; ++ks) wreg[nt][ks].load(wfrag_ptr(nt, ks));
   }
 
-  // Each work-group takes a contiguous range of work items: consecutive items
-  // continue along the same plane row, so the channel blocks it writes stay in
-  // the same few pages (scattering items over the grid makes nearly every
-  // store miss the address-translation cache).
+  // Item order: groups of kRowGroup plane rows; inside a group, column block
+  // by column block, and inside a column block row by row.  Each work-group
+  // takes a contiguous range of items, so it writes kRowGroup consecutive
+  // 128-byte rows of every channel block it touches one after the other
+  // (2 KB runs per channel instead of scattered lines) and stays in a few
+  // pages of the operand.
   const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
   const int64_t tile_begin = blockIdx.x * per_wg;
   const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
   if (tile_begin >= tile_end) return;
 
-  // plane position (row r, first column t0) of a work item, advanced in order
+  // plane position of a work item: row r, first column t0, and the row group
+  // [g0, g0 + gn) it belongs to; advanced in item order
   struct Pos {
-    int64_t r, t0;
+    int64_t r, t0, g0, gn;
   };
-  auto pos_of = [&](int64_t tile) { return Pos{tile / tiles_per_row, (tile % tiles_per_row) * kPairs}; };
+  auto group_rows = [&](int64_t g0) { return p.n_rows - g0 < kRowGroup ? p.n_rows - g0 : (int64_t)kRowGroup; };
+  auto pos_of = [&](int64_t tile) {
+    const int64_t g0 = tile / (kRowGroup * tiles_per_row) * kRowGroup;
+    const int64_t gn = group_rows(g0);
+    const int64_t rem = tile - g0 * tiles_per_row;
+    return Pos{g0 + rem % gn, rem / gn * kPairs, g0, gn};
+  };
   auto next_pos = [&](Pos q) {
-    q.t0 += kPairs;
-    if (q.t0 == p.ld) { q.t0 = 0; ++q.r; }
+    if (++q.r == q.g0 + q.gn) {
+      q.r = q.g0;
+      q.t0 += kPairs;
+      if (q.t0 == p.ld) {
+        q.t0 = 0;
+        q.g0 += kRowGroup;
+        q.gn = group_rows(q.g0);
+        q.r = q.g0;
+      }
+    }
     return q;
   };
 
