@@ -121,15 +121,11 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   constexpr bool kWeightsInRegs = (E == 2);
   using Op = Operand<T>;
   constexpr int kOpBytes = Op::BYTES;
-  constexpr int kStageBytes = kPairs * kOutRowF * 4;
-  constexpr int kLdsBytes = (2 * kOpBytes) > kStageBytes ? (2 * kOpBytes) : kStageBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float red[8][kPairs];
-  __shared__ float stat_mean[kPairs], stat_rstd[kPairs];
+  __shared__ __attribute__((aligned(16))) unsigned char n_ops[kOpBytes];   // normalised x
+  __shared__ __attribute__((aligned(16))) unsigned char z_ops[kOpBytes];   // normalised z
+  __shared__ __attribute__((aligned(16))) float stage[kPairs * kOutRowF];
+  __shared__ __attribute__((aligned(8))) float2 part[8][kPairs];          // per-group (mean, M2)
   __shared__ __attribute__((aligned(4))) uint8_t mask_lds[kPairs];
-  unsigned char *const n_ops = lds;               // normalised x
-  unsigned char *const z_ops = lds + kOpBytes;    // normalised z
-  float *const stage = reinterpret_cast<float *>(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,9 +163,17 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
 
   // ---- per-item loads (prefetched one item ahead) --------------------------
+  // Pairs outside the tile read a valid stand-in pair and count as masked.
   float xv[kXPer];
   ZUnit<T> zr[2];
   uint8_t mraw = 0;
+  auto pair_index = [&](int64_t blk, int64_t s0, int pr, bool &valid) -> int64_t {
+    const int64_t r = blk * 4 + (pr & 3), col = s0 + (pr >> 2);
+    valid = r < p.n_rows && col < p.n_cols;
+    const int64_t rr = r < p.n_rows ? r : p.n_rows - 1;
+    const int64_t cc = col < p.n_cols ? col : p.n_cols - 1;
+    return (p.row_off + rr) * p.n + p.col_off + cc;
+  };
   auto load_item = [&](int64_t tile) {
     const int64_t blk = tile / tiles_per_blk;
     const int64_t s0 = (tile % tiles_per_blk) * kCols;
@@ -178,68 +182,67 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
     const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
 #pragma unroll
     for (int c = 0; c < kXPer; ++c) xv[c] = xp[c * 64];
+    bool valid;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int qq = 32 * s + (tid >> 4);
-      const int64_t r = blk * 4 + (qq & 3), col = s0 + (qq >> 2);
-      if (r < p.n_rows && col < p.n_cols)
-        zr[s].load(zbytes + (((p.row_off + r) * p.n + p.col_off + col) * kCz + cg * 8) * E);
-      else
-        zr[s].zero();
+      const int64_t idx = pair_index(blk, s0, 32 * s + (tid >> 4), valid);
+      zr[s].load(zbytes + (idx * kCz + cg * 8) * E);
     }
-    if (tid < kPairs) {
-      const int64_t r = blk * 4 + (tid & 3), col = s0 + (tid >> 2);
-      mraw = (r < p.n_rows && col < p.n_cols) ? (p.mask[(p.row_off + r) * p.n + p.col_off + col] != 0) : 0;
-    }
+    const int64_t mi = pair_index(blk, s0, q, valid);
+    const uint8_t mb = p.mask[mi];
+    mraw = (valid && mb != 0) ? 1 : 0;
   };
 
   // Each work-group takes a contiguous range of work items, so consecutive
-  // items read neighbouring columns of every x channel plane and of z (few
-  // pages in the address-translation cache at a time).
+  // items read consecutive 32 KB blocks of x and neighbouring columns of z.
   const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
   const int64_t tile_begin = blockIdx.x * per_wg;
   const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
   int64_t tile = tile_begin;
   if (tile < tile_end) load_item(tile);
 
+  // Three barriers per item: (1) per-group LayerNorm partials written,
+  // (2) normalised operands written, (3) output stage written.  Every
+  // buffer written in one phase is last read two phases earlier.
   for (; tile < tile_end; ++tile) {
     const int64_t blk = tile / tiles_per_blk;
     const int64_t s0 = (tile % tiles_per_blk) * kCols;
 
-    // ---- output LayerNorm statistics (two passes, across the 8 groups) ----
-    float sum = 0.f;
+    // ---- output LayerNorm: exact per-thread partials over 16 channels,
+    //      merged per pair across the 8 groups (Chan et al.'s pairwise
+    //      update of mean and sum of squared deviations) -----------------------
+    {
+      float sum = 0.f;
 #pragma unroll
-    for (int c = 0; c < kXPer; ++c) sum += xv[c];
-    red[wave][q] = sum;
-    if (tid < kPairs) mask_lds[tid] = mraw;
-    __syncthreads();
-    if (tid < kPairs) {
-      float t = 0.f;
+      for (int c = 0; c < kXPer; ++c) sum += xv[c];
+      const float m = sum * (1.0f / kXPer);
+      float m2 = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) t += red[g][tid];
-      stat_mean[tid] = t * (1.0f / kC);
+      for (int c = 0; c < kXPer; ++c) { const float d = xv[c] - m; m2 += d * d; }
+      part[wave][q] = make_float2(m, m2);
+      if (wave == 0) mask_lds[q] = mraw;
     }
-    __syncthreads();
-    const float mean = stat_mean[q];
-    float sq = 0.f;
+    __syncthreads();   // (1)
+    {
+      float2 pg[8];
 #pragma unroll
-    for (int c = 0; c < kXPer; ++c) { xv[c] -= mean; sq += xv[c] * xv[c]; }
-    red[wave][q] = sq;
-    __syncthreads();
-    if (tid < kPairs) {
-      float t = 0.f;
+      for (int g = 0; g < 8; ++g) pg[g] = part[g][q];
+      float msum = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) t += red[g][tid];
-      stat_rstd[tid] = rsqrt_f32(t * (1.0f / kC) + p.eps);
-    }
-    __syncthreads();
-    const float rstd = stat_rstd[q];
+      for (int g = 0; g < 8; ++g) msum += pg[g].x;
+      const float mean = msum * (1.0f / 8);
+      float m2 = 0.f, dev = 0.f;
 #pragma unroll
-    for (int u = 0; u < kXPer / 8; ++u) {
-      float f[8];
+      for (int g = 0; g < 8; ++g) { m2 += pg[g].y; const float d = pg[g].x - mean; dev += d * d; }
+      const float var = (m2 + kXPer * dev) * (1.0f / kC);
+      const float rstd = rsqrt_f32(var + p.eps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = xv[8 * u + i] * rstd * gx[8 * u + i] + bx[8 * u + i];
-      Op::put(n_ops, q, xc0 / 8 + u, f);
+      for (int u = 0; u < kXPer / 8; ++u) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (xv[8 * u + i] - mean) * rstd * gx[8 * u + i] + bx[8 * u + i];
+        Op::put(n_ops, q, xc0 / 8 + u, f);
+      }
     }
 
     // ---- input LayerNorm of z (recomputed) for the gate --------------------
@@ -250,16 +253,16 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       float zs = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) zs += f[i];
-      const float zm = group_sum<16>(zs) * (1.0f / kCz);
+      const float zm = row_sum16(zs) * (1.0f / kCz);
       float zq = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { f[i] -= zm; zq += f[i] * f[i]; }
-      const float zrs = rsqrt_f32(group_sum<16>(zq) * (1.0f / kCz) + p.eps);
+      const float zrs = rsqrt_f32(row_sum16(zq) * (1.0f / kCz) + p.eps);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * zrs * gz[i] + bz[i];
       Op::put(z_ops, 32 * s + (tid >> 4), cg, f);
     }
-    __syncthreads();
+    __syncthreads();   // (2)
 
     // ---- prefetch the next item ----------------------------------------------
     if (tile + 1 < tile_end) load_item(tile + 1);
@@ -278,22 +281,22 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       Op::mma_at(ay, fo, n_ops, pq, unit);
       Op::mma_at(ag, fg, z_ops, pq, unit);
     }
-    const bool keep = mask_lds[pq] != 0;
-    __syncthreads();   // operands consumed; LDS becomes the output stage
 
     // ---- gate * projection * mask -> LDS stage -----------------------------
+    const bool keep = mask_lds[pq] != 0;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       f32x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * g4 + i;
-        v[i] = keep ? sigmoid_f32(ag[e]) * ay[e] : 0.f;
+        const float gated = sigmoid_f32(ag[e]) * ay[e];
+        v[i] = keep ? gated : 0.f;
       }
       const int o = o0 + acc_row(4 * g4, lane);
       *reinterpret_cast<f32x4 *>(stage + pq * kOutRowF + o) = v;
     }
-    __syncthreads();
+    __syncthreads();   // (3)
 
     // ---- stage -> HBM: whole pair rows, 16 bytes per lane ------------------
 #pragma unroll
@@ -305,7 +308,6 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
         *reinterpret_cast<f32x4 *>(p.out + (r * p.n_cols + col) * kCz + o4) =
             *reinterpret_cast<const f32x4 *>(stage + pp * kOutRowF + o4);
     }
-    __syncthreads();
   }
 }
 
