@@ -171,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   // valid stand-in pair and count as masked, so the code stays branch-free.
   const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
   ZUnit<T> raw[2];
-  bool keep[2];
+  uint8_t mbyte[2];   // mask bytes, tested only in the LayerNorm so that
+  bool mvalid[2];     // issuing the loads never waits for them
   auto pair_index = [&](int64_t r, int64_t t, bool &valid) -> int64_t {
     valid = t < p.k_len && r < p.n_rows;
     const int64_t rr = r < p.n_rows ? r : p.n_rows - 1;
@@ -187,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       bool valid;
       const int64_t idx = pair_index(q.r, q.t0 + pr, valid);
       raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
-      const uint8_t mb = p.mask[idx];
-      keep[s] = valid && mb != 0;
+      mbyte[s] = p.mask[idx];
+      mvalid[s] = valid;
     }
   };
 
@@ -208,8 +209,9 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) { f[i] -= mean; sq += f[i] * f[i]; }
       const float rstd = rsqrt_f32(row_sum16(sq) * (1.0f / kCz) + p.eps);
+      const bool keep = mvalid[s] && mbyte[s] != 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = keep[s] ? f[i] * rstd * g8[i] + b8[i] : 0.f;
+      for (int i = 0; i < 8; ++i) f[i] = keep ? f[i] * rstd * g8[i] + b8[i] : 0.f;
       const int pr = 32 * s + (tid >> 4);
       put_unit(zh_lds[buf] + pr * ROWB + swz<16>(pr, cg) * UNIT, f, T{});
     }

@@ -87,15 +87,25 @@ struct Operand<bf16_t> {
     *reinterpret_cast<u32x4 *>(base + off) = h;
     *reinterpret_cast<u32x4 *>(base + PLANE + off) = l;
   }
-  // acc += W * v over 16 k values (both terms)
-  __device__ static void mma_at(f32x16 &acc, const Frag<bf16_t> &w, const unsigned char *base, int q,
-                                int unit) {
+  // k-fragments of pair row q, 8-channel unit `unit`: hi and lo terms of the
+  // normalised x (n) and z (z) operands
+  struct Frags {
+    Frag<bf16_t> nh, nl, zh, zl;
+  };
+  __device__ static void read(Frags &f, const unsigned char *n, const unsigned char *z, int q, int unit) {
     const int off = q * ROWB + swz<16>(q, unit) * UNIT;
-    Frag<bf16_t> h, l;
-    h.load(base + off);
-    l.load(base + PLANE + off);
-    mma(acc, w, h);
-    mma(acc, w, l);
+    f.nh.load(n + off);
+    f.nl.load(n + PLANE + off);
+    f.zh.load(z + off);
+    f.zl.load(z + PLANE + off);
+  }
+  // ay += Wo * n, ag += Wg * z over 16 k values (both terms)
+  __device__ static void mma(f32x16 &ay, f32x16 &ag, const Frag<bf16_t> &wo, const Frag<bf16_t> &wg,
+                             const Frags &f) {
+    ::trimul::mma(ay, wo, f.nh);
+    ::trimul::mma(ag, wg, f.zh);
+    ::trimul::mma(ay, wo, f.nl);
+    ::trimul::mma(ag, wg, f.zl);
   }
 };
 
@@ -107,11 +117,18 @@ struct Operand<float> {
     reinterpret_cast<f32x4 *>(base + off)[0] = f32x4{f[0], f[1], f[2], f[3]};
     reinterpret_cast<f32x4 *>(base + off)[1] = f32x4{f[4], f[5], f[6], f[7]};
   }
-  __device__ static void mma_at(f32x16 &acc, const Frag<float> &w, const unsigned char *base, int q,
-                                int unit) {
-    Frag<float> v;
-    v.load(base + q * ROWB + swz<16>(q, unit) * UNIT);
-    mma(acc, w, v);
+  struct Frags {
+    Frag<float> n, z;
+  };
+  __device__ static void read(Frags &f, const unsigned char *n, const unsigned char *z, int q, int unit) {
+    const int off = q * ROWB + swz<16>(q, unit) * UNIT;
+    f.n.load(n + off);
+    f.z.load(z + off);
+  }
+  __device__ static void mma(f32x16 &ay, f32x16 &ag, const Frag<float> &wo, const Frag<float> &wg,
+                             const Frags &f) {
+    ::trimul::mma(ay, wo, f.n);
+    ::trimul::mma(ag, wg, f.z);
   }
 };
 
@@ -166,7 +183,8 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   // Pairs outside the tile read a valid stand-in pair and count as masked.
   float xv[kXPer];
   ZUnit<T> zr[2];
-  uint8_t mraw = 0;
+  uint8_t mbyte = 0;   // mask byte of pair q (tested only where it is used, so
+  bool mvalid = false; // that issuing the prefetch never waits for it)
   auto pair_index = [&](int64_t blk, int64_t s0, int pr, bool &valid) -> int64_t {
     const int64_t r = blk * 4 + (pr & 3), col = s0 + (pr >> 2);
     valid = r < p.n_rows && col < p.n_cols;
@@ -188,9 +206,8 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       const int64_t idx = pair_index(blk, s0, 32 * s + (tid >> 4), valid);
       zr[s].load(zbytes + (idx * kCz + cg * 8) * E);
     }
-    const int64_t mi = pair_index(blk, s0, q, valid);
-    const uint8_t mb = p.mask[mi];
-    mraw = (valid && mb != 0) ? 1 : 0;
+    mbyte = p.mask[pair_index(blk, s0, q, valid)];
+    mvalid = valid;
   };
 
   // Each work-group takes a contiguous range of work items, so consecutive
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
 #pragma unroll
       for (int c = 0; c < kXPer; ++c) { const float d = xv[c] - m; m2 += d * d; }
       part[wave][q] = make_float2(m, m2);
-      if (wave == 0) mask_lds[q] = mraw;
+      if (wave == 0) mask_lds[q] = (mvalid && mbyte != 0) ? 1 : 0;
     }
     __syncthreads();   // (1)
     {
@@ -272,14 +289,20 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) { ay[e] = 0.f; ag[e] = 0.f; }
     const int pq = ph + (lane & 31);   // this lane's pair column
+    // operand fragments are read one k step ahead of the matrix-core
+    // instructions that use them
+    typename Op::Frags fr[2];
+    Op::read(fr[0], n_ops, z_ops, pq, lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) Op::read(fr[(ks + 1) & 1], n_ops, z_ops, pq, 2 * (ks + 1) + (lane >> 5));
       Frag<T> fo, fg;
       if constexpr (kWeightsInRegs) { fo = wo[ks]; fg = wg[ks]; }
       else { fo.load(wptr(Wo, ks)); fg.load(wptr(Wg, ks)); }
-      const int unit = 2 * ks + (lane >> 5);
-      Op::mma_at(ay, fo, n_ops, pq, unit);
-      Op::mma_at(ag, fg, z_ops, pq, unit);
+      // keep the reads of step ks+1 ahead of this step's products
+      __builtin_amdgcn_sched_barrier(0);
+      Op::mma(ay, ag, fo, fg, fr[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- gate * projection * mask -> LDS stage -----------------------------
