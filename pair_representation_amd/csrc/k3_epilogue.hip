@@ -11,7 +11,7 @@
 // while the current one is processed.
 //  - x: thread (pair p = tid % 64, channel group tid / 64) holds 16 channels;
 //    output LayerNorm statistics are combined over the 8 groups in LDS.
-//  - z is re-read (16 lanes per pair, 16-lane shuffle reductions) and
+//  - z is re-read (16 lanes per pair, 16-lane DPP reductions) and
 //    re-normalised for the gate.
 //  - Both normalised operands go to LDS as matrix-core B operands; in bf16
 //    mode each is split into hi + lo bf16 terms (hi = bf16(v),
@@ -19,8 +19,8 @@
 //    products keep fp32-level accuracy.
 //  - Wave w computes output channels 32*(w%4) .. +31 of both the projection
 //    and the gate for pairs 32*(w/4) .. +31, so the final product is formed in
-//    registers; it is staged through LDS and stored as whole 512-byte pair
-//    rows.  bf16 weight fragments stay in registers for the whole pass.
+//    registers and stored from there, 16 bytes (4 channels) per lane.  bf16
+//    weight fragments stay in registers for the whole pass.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,7 +31,6 @@ namespace {
 constexpr int kPairs = 64;
 constexpr int kRows = 4, kCols = 16;  // work-item shape
 constexpr int kThreads = 512;
-constexpr int kOutRowF = kCz + 4;     // staged output row (floats), padded against bank conflicts
 constexpr int kXPer = kC / 8;         // x channels per thread
 
 template <typename T>
@@ -140,7 +139,6 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   constexpr int kOpBytes = Op::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char n_ops[kOpBytes];   // normalised x
   __shared__ __attribute__((aligned(16))) unsigned char z_ops[kOpBytes];   // normalised z
-  __shared__ __attribute__((aligned(16))) float stage[kPairs * kOutRowF];
   __shared__ __attribute__((aligned(8))) float2 part[8][kPairs];          // per-group (mean, M2)
   __shared__ __attribute__((aligned(4))) uint8_t mask_lds[kPairs];
 
@@ -218,9 +216,11 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   int64_t tile = tile_begin;
   if (tile < tile_end) load_item(tile);
 
-  // Three barriers per item: (1) per-group LayerNorm partials written,
-  // (2) normalised operands written, (3) output stage written.  Every
-  // buffer written in one phase is last read two phases earlier.
+  // Two barriers per item: (1) per-group LayerNorm partials written,
+  // (2) normalised operands written.  The partials of the next item are
+  // written after (2), when every wave has read the current ones; the
+  // operands of the next item after its (1), when every wave has finished
+  // this item's products.
   for (; tile < tile_end; ++tile) {
     const int64_t blk = tile / tiles_per_blk;
     const int64_t s0 = (tile % tiles_per_blk) * kCols;
@@ -240,6 +240,10 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       if (wave == 0) mask_lds[q] = (mvalid && mbyte != 0) ? 1 : 0;
     }
     __syncthreads();   // (1)
+    // mask of this lane's output pair, read before (2): the next item's
+    // mask is written after it
+    const int pq = ph + (lane & 31);   // this lane's pair column
+    const bool keep = mask_lds[pq] != 0;
     {
       float2 pg[8];
 #pragma unroll
@@ -288,7 +292,6 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
     f32x16 ay, ag;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { ay[e] = 0.f; ag[e] = 0.f; }
-    const int pq = ph + (lane & 31);   // this lane's pair column
     // operand fragments are read one k step ahead of the matrix-core
     // instructions that use them
     typename Op::Frags fr[2];
@@ -305,31 +308,25 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- gate * projection * mask -> LDS stage -----------------------------
-    const bool keep = mask_lds[pq] != 0;
+    // ---- gate * projection * mask -> HBM ----------------------------------
+    // Accumulator registers 4g..4g+3 of a lane are 4 consecutive output
+    // channels of its pair: one 16-byte store each; the four stores of a lane
+    // and its partner lane (lane ^ 32) cover 32 consecutive channels (128
+    // bytes) of the pair's output row.
+    const int64_t r = blk * 4 + (pq & 3), col = s0 + (pq >> 2);
+    if (r < p.n_rows && col < p.n_cols) {
+      float *const orow = p.out + (r * p.n_cols + col) * kCz + o0;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4 v;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * g4 + i;
-        const float gated = sigmoid_f32(ag[e]) * ay[e];
-        v[i] = keep ? gated : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g4 + i;
+          const float gated = sigmoid_f32(ag[e]) * ay[e];
+          v[i] = keep ? gated : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(orow + acc_row(4 * g4, lane)) = v;
       }
-      const int o = o0 + acc_row(4 * g4, lane);
-      *reinterpret_cast<f32x4 *>(stage + pq * kOutRowF + o) = v;
-    }
-    __syncthreads();   // (3)
-
-    // ---- stage -> HBM: whole pair rows, 16 bytes per lane ------------------
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = i * kThreads + tid;
-      const int pp = u >> 5, o4 = (u & 31) * 4;
-      const int64_t r = blk * 4 + (pp & 3), col = s0 + (pp >> 2);
-      if (r < p.n_rows && col < p.n_cols)
-        *reinterpret_cast<f32x4 *>(p.out + (r * p.n_cols + col) * kCz + o4) =
-            *reinterpret_cast<const f32x4 *>(stage + pp * kOutRowF + o4);
     }
   }
 }
