@@ -36,6 +36,7 @@ namespace trimul {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kLoadWaves = 4;   // waves that issue the operand loads (one per SIMD)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
@@ -50,11 +51,11 @@ struct K2Cfg {
   static constexpr int WM = BM / 2, WN = BN / 4;
   static constexpr int MT = WM / 32, NT = WN / 32;
   static constexpr int KS = BK / 16;           // 16-wide k steps per k-tile
-  static constexpr int A_I = BM * RU / kThreads;    // 1 KB load instructions per wave (A)
-  static constexpr int B_I = BN * RU / kThreads;
+  static constexpr int A_I = BM * RU / (64 * kLoadWaves);   // 1 KB load instructions per loading wave (A)
+  static constexpr int B_I = BN * RU / (64 * kLoadWaves);
   static constexpr int STAGE = (BM + BN) * ROWB;
   static_assert(RU == 8, "LDS rows are 8 units wide");
-  static_assert(A_I * kThreads == BM * RU && B_I * kThreads == BN * RU, "load split");
+  static_assert(A_I * 64 * kLoadWaves == BM * RU && B_I * 64 * kLoadWaves == BN * RU, "load split");
 };
 
 // Physical 16-byte unit of logical unit u in LDS row r.  A 128-byte row is
@@ -116,9 +117,12 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   const int m0 = tm * BM, n0 = tn * BN;
 
   // ---- direct-to-LDS loads --------------------------------------------
-  // Load instruction i of this wave fills LDS block q = i*8 + wave (1 KB =
-  // 8 rows of 128 bytes); lane l fills row q*8 + l/8, physical unit l%8,
-  // which holds logical unit k2_swz(row, l%8) (the swizzle is an involution).
+  // Only waves 0 .. kLoadWaves-1 (one per SIMD) issue loads: a wave stalls
+  // while the texture path accepts its load instructions, and the other wave
+  // of its SIMD keeps the matrix core busy meanwhile.  Load instruction i of
+  // a loading wave fills LDS block q = i*kLoadWaves + wave (1 KB = 8 rows of
+  // 128 bytes); lane l fills row q*8 + l/8, physical unit l%8, which holds
+  // logical unit k2_swz(row, l%8) (the swizzle is an involution).
   const int lrow = lane >> 3;
   auto issue_loads = [&](int ci, int kt, int buf) {
     // The k-tile is one contiguous run of one channel block of each operand
@@ -138,16 +142,17 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
     const int a_row0 = m0 % kOpRows, b_row0 = n0 % kOpRows;
     unsigned char *sa = lds + buf * C::STAGE;
     unsigned char *sb = sa + BM * C::ROWB;
+    if (wave >= kLoadWaves) return;
 #pragma unroll
     for (int i = 0; i < C::A_I; ++i) {
-      const int q = i * 8 + wave;
+      const int q = i * kLoadWaves + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((a_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
-      const int q = i * 8 + wave;
+      const int q = i * kLoadWaves + wave;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((b_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, off, 0, 0, 0);
