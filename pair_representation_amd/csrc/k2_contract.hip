@@ -31,6 +31,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace trimul {
 
 namespace {
@@ -72,6 +74,13 @@ __device__ __forceinline__ void lds_frag(Frag<T> &f, const unsigned char *row_ba
 #pragma unroll
   for (int u = 0; u < UPF; ++u)
     dst[u] = *reinterpret_cast<const u32x4 *>(row_base + k2_swz(row, g * UPF + u) * 16);
+}
+
+// Number of 32-wide blocks of a wave's range that hold at least one valid
+// row, given `valid` rows from the start of the range; 0 .. cap.
+__device__ __forceinline__ int clamp_count(int valid, int cap) {
+  const int c = (valid + 31) / 32;
+  return valid <= 0 ? 0 : (c < cap ? c : cap);
 }
 
 __device__ __forceinline__ void wait_vm0() {
@@ -187,7 +196,16 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // issued; scheduling barriers keep the compiler from sinking the reads next
   // to their consumers, so the LDS latency hides behind a whole step of
   // matrix-core work and the matrix core stays fed.
-  auto compute = [&](int buf, bool with_loads) {
+  //
+  // In a tile at the ragged edge of the output, 32-row (32-column) blocks of
+  // a wave that lie entirely past M (N) are padding: their fragment reads and
+  // products are skipped (wave-uniform counts), which makes the edge tiles of
+  // a ragged N cheaper; full tiles take a path without these checks.
+  const int mt_act = clamp_count((int)(p.M - m0) - wm * C::WM, C::MT);
+  const int nt_act = clamp_count((int)(p.N - n0) - wn * C::WN, C::NT);
+  const bool full = (mt_act == C::MT) && (nt_act == C::NT);
+  auto compute = [&](int buf, auto whole) {
+    constexpr bool kWhole = decltype(whole)::value;
     const unsigned char *sa = lds + buf * C::STAGE;
     const unsigned char *sb = sa + BM * C::ROWB;
     Frag<T> af[2][C::MT], bfr[2][C::NT];
@@ -195,11 +213,13 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
       const int g = 2 * ks + (lane >> 5);  // 8-element group of this lane
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
+        if (!kWhole && mt >= mt_act) continue;
         const int row = wm * C::WM + mt * 32 + (lane & 31);
         lds_frag(af[slot][mt], sa + row * C::ROWB, row, g);
       }
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
+        if (!kWhole && nt >= nt_act) continue;
         const int row = wn * C::WN + nt * 32 + (lane & 31);
         lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, g);
       }
@@ -213,21 +233,26 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) mma(acc[mt][nt], af[cur][mt], bfr[cur][nt]);
+        for (int nt = 0; nt < C::NT; ++nt)
+          if (kWhole || (mt < mt_act && nt < nt_act)) mma(acc[mt][nt], af[cur][mt], bfr[cur][nt]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    (void)with_loads;
   };
-
-  for (int it = 0; it + 1 < total_kt; ++it) {
-    const int buf = it & 1;
-    issue_loads(ci, kt, buf ^ 1);
-    advance();
-    compute(buf, true);
-    wait_vm0();
-    __syncthreads();
-  }
-  if (total_kt > 0) compute((total_kt - 1) & 1, false);
+  auto k_loop = [&](auto whole) {
+    for (int it = 0; it + 1 < total_kt; ++it) {
+      const int buf = it & 1;
+      issue_loads(ci, kt, buf ^ 1);
+      advance();
+      compute(buf, whole);
+      wait_vm0();
+      __syncthreads();
+    }
+    if (total_kt > 0) compute((total_kt - 1) & 1, whole);
+  };
+  if (full)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
 
   // ---- write / accumulate x -------------------------------------------
   // The four accumulator registers 4g..4g+3 of a lane are rows 4k..4k+3 of
