@@ -83,6 +83,13 @@ __device__ __forceinline__ int clamp_count(int valid, int cap) {
   return valid <= 0 ? 0 : (c < cap ? c : cap);
 }
 
+// Rows of a tile covered by 32-row blocks that hold a valid row: valid rows
+// rounded up to 32, at most cap.
+__device__ __forceinline__ int row_extent(int valid, int cap) {
+  const int r = (valid + 31) / 32 * 32;
+  return r < cap ? r : cap;
+}
+
 __device__ __forceinline__ void wait_vm0() {
   // s_waitcnt vmcnt(0), other counters unconstrained
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -133,6 +140,10 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // 128 bytes); lane l fills row q*8 + l/8, physical unit l%8, which holds
   // logical unit k2_swz(row, l%8) (the swizzle is an involution).
   const int lrow = lane >> 3;
+  // operand rows of this tile that any product uses: up to the end of the
+  // last 32-row block holding a valid row (see the edge-tile skipping below)
+  const int a_rows = row_extent((int)(p.M - m0), BM);
+  const int b_rows = row_extent((int)(p.N - n0), BN);
   auto issue_loads = [&](int ci, int kt, int buf) {
     // The k-tile is one contiguous run of one channel block of each operand
     // (256 rows x 64 columns per block; a BK-wide k-tile is columns kk ..
@@ -155,6 +166,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 #pragma unroll
     for (int i = 0; i < C::A_I; ++i) {
       const int q = i * kLoadWaves + wave;
+      if (q * 8 >= a_rows) continue;   // rows only skipped blocks would read
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((a_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, off, 0, 0, 0);
@@ -162,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
       const int q = i * kLoadWaves + wave;
+      if (q * 8 >= b_rows) continue;
       const int lunit = k2_swz(q * 8 + lrow, lane & 7);
       const int off = ((b_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, off, 0, 0, 0);
