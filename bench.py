@@ -111,6 +111,69 @@ def cpu_baseline(work, block_rows):
     }
 
 
+def bench_tile(work, args, dev):
+    """The per-device step of the tiled form: operand chunks for one tile
+    (K1), the k-contraction over all chunks in ring order (K2) and the
+    epilogue (K3), timed per kernel with HIP events on the launch stream.
+    The rate is the tile's pair updates over K2 + K3 (the chunks of a real
+    grid arrive from other devices); K1 is reported separately."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    t = work.tile
+    log(f"[bench] generating {work.name} (N={work.n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    ld = (t["chunk"] + 63) // 64 * 64
+    rows, cols = t["n_rows"], t["n_cols"]
+    res = {}
+    for d, name in ((pra.OUTGOING, "outgoing"), (pra.INCOMING, "incoming")):
+        a_ops = [pra.new_operand(rows, ld, w.torch_dtype, dev) for _ in range(t["n_chunks"])]
+        b_ops = [pra.new_operand(cols, ld, w.torch_dtype, dev) for _ in range(t["n_chunks"])]
+        x = pra.new_xacc(rows, cols, dev)
+        out = torch.empty((rows, cols, C_Z), dtype=torch.float32, device=dev)
+        chunks = [(c * t["chunk"], t["chunk"], a_ops[c], b_ops[c]) for c in range(t["n_chunks"])]
+
+        def run(ev=None):
+            if ev is not None:
+                ev[0].record()
+            for c in range(t["n_chunks"]):
+                pra.tile_operands(w, d, z, mask, t["row_off"], rows, t["col_off"], cols, c * t["chunk"],
+                                  t["chunk"], ld, a_out=a_ops[c], b_out=b_ops[c])
+            if ev is not None:
+                ev[1].record()
+            pra.tile(w, work.n, t["row_off"], rows, t["col_off"], cols, chunks, pra.TILE_FIRST, x)
+            if ev is not None:
+                ev[2].record()
+            pra.tile(w, work.n, t["row_off"], rows, t["col_off"], cols, [], pra.TILE_LAST, x, z, mask, out)
+            if ev is not None:
+                ev[3].record()
+
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(args.steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            run(ev)
+            evs.append(ev)
+        torch.cuda.synchronize()
+        k = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / len(evs) * 1e-3 for i in range(3)]
+        flops = 2.0 * rows * cols * t["chunk"] * t["n_chunks"] * C
+        res[name] = {"tile_pair_updates_per_s": rows * cols / (k[1] + k[2]),
+                     "k1_operands_ms": k[0] * 1e3, "k2_contract_ms": k[1] * 1e3, "k3_epilogue_ms": k[2] * 1e3,
+                     "k2_TFLOP/s": flops / k[1] / 1e12, "k2_frac": flops / k[1] / 1e12 / PEAK_BF16_TFLOPS}
+        del a_ops, b_ops, x, out, chunks
+        torch.cuda.empty_cache()
+    both = 2 * rows * cols / sum(res[nm]["k2_contract_ms"] + res[nm]["k3_epilogue_ms"] for nm in res) * 1e3
+    return {"metric": "TriMul tile pair-updates/s over contraction + epilogue (operand chunks timed apart)",
+            "value": both, "unit": "pair-updates/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": work.dtype, "data": "synthetic",
+            "config": {"workload": work.name, "n": work.n, "tile": t}, "directions": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +207,9 @@ def main():
                           "launches": 3}), flush=True)
         return
     work = wl.WORKLOADS[args.workload]
+    if work.tile:
+        print(json.dumps(bench_tile(work, args, dev)), flush=True)
+        return
     n = work.n
     log(f"[bench] generating {work.name} (N={n}) on the GPU")
     z, mask, wts = wl.make_inputs(work, dev)
@@ -212,6 +278,11 @@ def main():
             durs["k2"].append(ev[d][1].elapsed_time(ev[d][2]) * 1e-3)
             durs["k3"].append(ev[d][2].elapsed_time(ev[d][3]) * 1e-3)
     avg = {k: sum(v) / len(v) for k, v in durs.items()}
+    per_dir = {}
+    for d, name in ((0, "outgoing"), (1, "incoming")):
+        t_dir = [ev[d][0].elapsed_time(ev[d][3]) * 1e-3 for ev in all_ev]
+        per_dir[name] = {"pair_updates_per_s": n * n / (sum(t_dir) / len(t_dir)),
+                         "ms_median": 1e3 * sorted(t_dir)[len(t_dir) // 2], "ms_min": 1e3 * min(t_dir)}
 
     pairs = n * n
     k2_flops = 2.0 * n * n * n * C
@@ -259,6 +330,7 @@ def main():
                             "TFLOP/s": K3_FLOPS_PER_PAIR * pairs / avg["k3"] / 1e12},
             "per_kernel_loop_ms_per_step": t_kern * 1e3,
         },
+        "per_direction": per_dir,
         "cpu_baseline": None,
     }
     del ws, out_o, out_i, z, mask
