@@ -185,7 +185,7 @@ def main():
                     help="copy: run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(collectives and sharding are out of scope); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
