@@ -7,22 +7,22 @@
 // Work-group tile BM x BN of one channel, eight waves (two per SIMD) in a
 // 2 x 4 layout, each wave a (BM/2) x (BN/4) block of 32 x 32 matrix-core
 // accumulators; the two waves of a SIMD hide each other's LDS and barrier
-// latency.  The
-// k-loop walks the chunks in the order given (a ring's delivery order) and,
-// inside each chunk, BK-wide k-tiles.
+// latency.  The k-loop walks the chunks in the order given (a ring's
+// delivery order) and, inside each chunk, BK-wide k-tiles.
 //
 // Operand staging: buffer loads that write LDS directly (no register
 // staging), two LDS stages, one barrier per k-tile: the loads of k-tile t+1
-// are in flight while k-tile t is on the matrix cores.  Each load instruction
-// fills 1 KB of LDS (64 lanes x 16 bytes at consecutive addresses), so the
-// XOR swizzle of 16-byte units inside a row (unit u of row r stored at
-// u ^ ((r / 2) % 8)) is applied on the global side: a lane fetches the
-// logical unit that belongs in its LDS slot.  In the operand layout (see
-// operand_offset) a k-tile of one channel is a single contiguous 32 KB run;
-// rows past the operand's end are padding rows of the last 256-row block and
-// only feed output rows/columns that are never stored.  k-fragments are read
-// from LDS one 16-wide k step ahead of the matrix-core instructions that
-// consume them.
+// are in flight while k-tile t is on the matrix cores.  One wave per SIMD
+// issues them.  Each load instruction fills 1 KB of LDS (64 lanes x 16 bytes
+// at consecutive addresses), so the XOR swizzle of 16-byte units inside a row
+// (unit u of row r stored at u ^ ((r / 2) % 8)) is applied on the global
+// side: a lane fetches the logical unit that belongs in its LDS slot.  In the
+// operand layout (see operand_offset) a k-tile of one channel is a single
+// contiguous 32 KB run; rows past the operand's end are padding rows of the
+// last 256-row block and only feed output rows/columns that are never stored
+// (in edge tiles, whole 32-row blocks of padding are skipped).  k-fragments
+// are read from LDS one 16-wide k step ahead of the matrix-core instructions
+// that consume them.
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
