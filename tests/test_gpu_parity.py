@@ -175,10 +175,13 @@ def test_operand_planes(dev, dtype, direction):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("m_rows,n_cols,klen", [(1, 1, 1), (40, 300, 77), (256, 256, 256), (300, 129, 515)])
+@pytest.mark.parametrize("m_rows,n_cols,klen", [(1, 1, 1), (40, 300, 77), (256, 256, 256), (300, 129, 515),
+                                                 (277, 300, 70), (21, 533, 64), (513, 31, 33)])
 def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     """Contraction kernel fed the oracle's operands directly (uploaded, exact in
-    the storage dtype) vs their float64 contraction."""
+    the storage dtype) vs their float64 contraction.  The shapes include edge
+    tiles with a few valid rows or columns past a 256 boundary (277 = 256 + 21,
+    533 = 512 + 21, 513) and single short tiles (21, 31)."""
     r = np.random.default_rng(m_rows * 7 + n_cols)
     ld = (klen + 63) // 64 * 64
     a = r.standard_normal((128, m_rows, klen))
@@ -198,7 +201,7 @@ def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     Bb = pra.planar_to_operand(B.to(dev))
     pra.tile(w, n, 0, m_rows, 0, n_cols, [(0, klen, Ab, Bb)], pra.TILE_FIRST, x)
     torch.cuda.synchronize()
-    ref = np.einsum("dik,djk->dij", a, b)
+    ref = np.matmul(a, b.transpose(0, 2, 1))
     e = rel_err(pra.xacc_to_planar(x, m_rows, n_cols).cpu().double().numpy(), ref)
     print(f"  contraction {dtype} {m_rows}x{n_cols}x{klen}: {e:.3e}")
     assert e <= 1e-5
