@@ -7,7 +7,8 @@
 // Work-group tile BM x BN of one channel, eight waves (two per SIMD) in a
 // 2 x 4 layout, each wave a (BM/2) x (BN/4) block of 32 x 32 matrix-core
 // accumulators; the two waves of a SIMD hide each other's LDS and barrier
-// latency.  The k-loop walks the chunks in the order given (a ring's
+// latency.  bf16: 256 x 384 x 64 (wave tile 128 x 96: 192 accumulator
+// registers, two 80 KB LDS stages); fp32: 128 x 128 x 32.  The k-loop walks the chunks in the order given (a ring's
 // delivery order) and, inside each chunk, BK-wide k-tiles.
 //
 // Operand staging: buffer loads that write LDS directly (no register
@@ -21,8 +22,10 @@
 // contiguous 32 KB run; rows past the operand's end are padding rows of the
 // last 256-row block and only feed output rows/columns that are never stored
 // (in edge tiles, whole 32-row blocks of padding are skipped).  k-fragments
-// are read from LDS one 16-wide k step ahead of the matrix-core instructions
-// that consume them.
+// are read from LDS ahead of the matrix-core instructions that consume them:
+// B fragments a whole 16-wide k step ahead (two register sets), A fragments
+// one at a time, each re-read for the next step as soon as the products of
+// the current step that use it have been issued (one register set).
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
@@ -51,6 +54,10 @@ struct K2Cfg {
   static constexpr int ROWB = BK * E;          // bytes per LDS row
   static constexpr int RU = ROWB / 16;         // 16-byte units per row
   static constexpr int WM = BM / 2, WN = BN / 4;
+  static_assert(kOpRows % 8 == 0 && BM <= kOpRows, "an A tile lies in one 256-row block");
+  static_assert(BN <= 2 * kOpRows, "a B tile spans at most two 256-row blocks");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "tiles start at row 0 or 128 of a 256-row block");
+  static_assert(kLoadWaves * 8 == 32, "load instruction i covers rows 32*i + 8*wave .. +7");
   static constexpr int MT = WM / 32, NT = WN / 32;
   static constexpr int KS = BK / 16;           // 16-wide k steps per k-tile
   static constexpr int A_I = BM * RU / (64 * kLoadWaves);   // 1 KB load instructions per loading wave (A)
@@ -140,11 +147,18 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // 128 bytes); lane l fills row q*8 + l/8, physical unit l%8, which holds
   // logical unit k2_swz(row, l%8) (the swizzle is an involution).
   const int lrow = lane >> 3;
+  // Lane part of every load offset: row lrow of the 8-row group, logical
+  // unit k2_swz(q*8 + lrow, lane % 8).  With q = i*kLoadWaves + wave and
+  // kLoadWaves even, (q*8 + lrow)/2 % 8 = 4*(wave % 2) + lrow/2: the unit is
+  // the same for every load instruction of a wave, and the rest of the
+  // offset (row group, k) is wave-uniform (the scalar offset).
+  static_assert(kLoadWaves % 2 == 0, "load groups of one wave share a swizzle");
+  const int lane_off = lrow * kOpCols * (int)sizeof(T) + (((lane & 7) ^ (4 * (wave & 1) + (lrow >> 1))) * 16);
   // operand rows of this tile that any product uses: up to the end of the
   // last 32-row block holding a valid row (see the edge-tile skipping below)
   const int a_rows = row_extent((int)(p.M - m0), BM);
   const int b_rows = row_extent((int)(p.N - n0), BN);
-  auto issue_loads = [&](int ci, int kt, int buf) {
+  auto issue_loads = [&](int ci, int kt, int buf) __attribute__((always_inline)) {
     // The k-tile is one contiguous run of one channel block of each operand
     // (256 rows x 64 columns per block; a BK-wide k-tile is columns kk ..
     // kk+BK-1 of it, rows m0 % 256 ..).
@@ -152,33 +166,49 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
     const int64_t kcol = (int64_t)kt * BK;
     const int64_t cb = kcol / kOpCols;
     const int kk = (int)(kcol % kOpCols);
-    // tiles never straddle a 256-row block (BM, BN divide 256)
+    // An A tile lies in one 256-row block; a B tile (384 rows) in at most
+    // two consecutive ones.  Each 8-row load group lies in one block and is
+    // addressed through that block's own buffer descriptor.
+    const int64_t blk_step = (ld / kOpCols) * kC * kOpBlock * C::E;   // bytes between 256-row blocks
     const int64_t a_blk = ((int64_t)(m0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
     const int64_t b_blk = ((int64_t)(n0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
     const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + a_blk * kOpBlock * C::E;
     const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + b_blk * kOpBlock * C::E;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
-    const int a_row0 = m0 % kOpRows, b_row0 = n0 % kOpRows;
     unsigned char *sa = lds + buf * C::STAGE;
     unsigned char *sb = sa + BM * C::ROWB;
     if (wave >= kLoadWaves) return;
+    // Load instruction i of this wave covers tile rows 32*i + 8*wave .. +7,
+    // i.e. rows r0 + 32*i + 8*wave of the first block: with r0 (the tile's
+    // first row inside its block, 0 or 128) a compile-time constant, the
+    // block of every instruction is known at compile time.
+    auto load_side = [&](auto r0c, auto ni, const unsigned char *base, unsigned char *dst, int valid_rows)
+        __attribute__((always_inline)) {
+      constexpr int r0 = decltype(r0c)::value;
+      constexpr int NI = decltype(ni)::value;
+      const __amdgpu_buffer_rsrc_t r_lo =
+          __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t r_hi =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(base + blk_step), (short)0, (int)(kOpBlock * C::E), kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < C::A_I; ++i) {
-      const int q = i * kLoadWaves + wave;
-      if (q * 8 >= a_rows) continue;   // rows only skipped blocks would read
-      const int lunit = k2_swz(q * 8 + lrow, lane & 7);
-      const int off = ((a_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + q * 1024), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_I; ++i) {
-      const int q = i * kLoadWaves + wave;
-      if (q * 8 >= b_rows) continue;
-      const int lunit = k2_swz(q * 8 + lrow, lane & 7);
-      const int off = ((b_row0 + q * 8 + lrow) * kOpCols + kk) * C::E + lunit * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + q * 1024), 16, off, 0, 0, 0);
-    }
+      for (int i = 0; i < NI; ++i) {
+        const int q = i * kLoadWaves + wave;
+        if (q * 8 >= valid_rows) continue;   // rows only skipped blocks would read
+        constexpr int kBlockRows = kOpRows;
+        const bool upper = r0 + 32 * i >= kBlockRows;   // folded per unrolled i
+        const int r = (r0 + q * 8) % kBlockRows;
+        const int soff = (r * kOpCols + kk) * C::E;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(upper ? r_hi : r_lo, (lds_void *)(dst + q * 1024), 16, lane_off,
+                                                 soff, 0, 0);
+      }
+    };
+    using R0 = std::integral_constant<int, 0>;
+    using R128 = std::integral_constant<int, 128>;
+    using NA = std::integral_constant<int, C::A_I>;
+    using NB = std::integral_constant<int, C::B_I>;
+    if (m0 % kOpRows == 0) load_side(R0{}, NA{}, A, sa, a_rows);
+    else load_side(R128{}, NA{}, A, sa, a_rows);
+    if (n0 % kOpRows == 0) load_side(R0{}, NB{}, B, sb, b_rows);
+    else load_side(R128{}, NB{}, B, sb, b_rows);
   };
 
   f32x16 acc[C::MT][C::NT];
@@ -217,41 +247,45 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   const int mt_act = clamp_count((int)(p.M - m0) - wm * C::WM, C::MT);
   const int nt_act = clamp_count((int)(p.N - n0) - wn * C::WN, C::NT);
   const bool full = (mt_act == C::MT) && (nt_act == C::NT);
-  auto compute = [&](int buf, auto whole) {
+  auto compute = [&](int buf, auto whole) __attribute__((always_inline)) {
     constexpr bool kWhole = decltype(whole)::value;
     const unsigned char *sa = lds + buf * C::STAGE;
     const unsigned char *sb = sa + BM * C::ROWB;
-    Frag<T> af[2][C::MT], bfr[2][C::NT];
-    auto read_frags = [&](int ks, int slot) {
-      const int g = 2 * ks + (lane >> 5);  // 8-element group of this lane
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        if (!kWhole && mt >= mt_act) continue;
-        const int row = wm * C::WM + mt * 32 + (lane & 31);
-        lds_frag(af[slot][mt], sa + row * C::ROWB, row, g);
-      }
+    Frag<T> af[C::MT], bfr[2][C::NT];
+    const int g_lane = lane >> 5;   // which 8-element half of a 16-wide k step
+    auto read_a = [&](int ks, int mt) __attribute__((always_inline)) {
+      const int row = wm * C::WM + mt * 32 + (lane & 31);
+      lds_frag(af[mt], sa + row * C::ROWB, row, 2 * ks + g_lane);
+    };
+    auto read_b = [&](int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
         if (!kWhole && nt >= nt_act) continue;
         const int row = wn * C::WN + nt * 32 + (lane & 31);
-        lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, g);
+        lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, 2 * ks + g_lane);
       }
     };
-    read_frags(0, 0);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      if (kWhole || mt < mt_act) read_a(0, mt);
+    read_b(0, 0);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < C::KS) read_frags(ks + 1, cur ^ 1);
+      if (ks + 1 < C::KS) read_b(ks + 1, cur ^ 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+      for (int mt = 0; mt < C::MT; ++mt) {
+        if (!kWhole && mt >= mt_act) continue;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
-          if (kWhole || (mt < mt_act && nt < nt_act)) mma(acc[mt][nt], af[cur][mt], bfr[cur][nt]);
-      __builtin_amdgcn_sched_barrier(0);
+          if (kWhole || nt < nt_act) mma(acc[mt][nt], af[mt], bfr[cur][nt]);
+        if (ks + 1 < C::KS) read_a(ks + 1, mt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
-  auto k_loop = [&](auto whole) {
+  auto k_loop = [&](auto whole) __attribute__((always_inline)) {
     for (int it = 0; it + 1 < total_kt; ++it) {
       const int buf = it & 1;
       issue_loads(ci, kt, buf ^ 1);
@@ -298,16 +332,16 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   const int64_t bk = (dtype == TRIMUL_BF16) ? 64 : 32;
-  const int64_t bn = (dtype == TRIMUL_BF16) ? 256 : 128;
-  const int64_t bm = bn;
+  const int64_t bm = (dtype == TRIMUL_BF16) ? 256 : 128;
+  const int64_t bn = (dtype == TRIMUL_BF16) ? 384 : 128;
   for (int c = 0; c < a.n_chunks; ++c) a.ch[c].ktiles = (int32_t)((a.ch[c].k_len + bk - 1) / bk);
   const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * kC;
-  // resident work-groups: one per CU for bf16 (128 KB of LDS), two for fp32
+  // resident work-groups: one per CU for bf16 (160 KB of LDS), two for fp32
   const int per_cu = (dtype == TRIMUL_BF16) ? 1 : 2;
   a.slots = (device_cu_count() * per_cu + kXcds - 1) / kXcds * kXcds;
   const int64_t grid = (tiles + a.slots - 1) / a.slots * a.slots;
   if (dtype == TRIMUL_BF16)
-    hipLaunchKernelGGL((k2_contract<bf16_t, 256, 256, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k2_contract<bf16_t, 256, 384, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((k2_contract<float, 128, 128, 32>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

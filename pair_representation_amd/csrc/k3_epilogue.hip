@@ -4,12 +4,15 @@
 // channels, see x_offset) and the
 // pair tensor, writing fp32 out[r][s][e].
 //
-// Work item: 64 pairs = 4 consecutive rows x 16 consecutive columns, pair
-// index p = 4*jj + ii, which is also the order of one channel's 64 values in
-// x (256 contiguous bytes).  512 threads = 8 waves (two per SIMD), persistent
+// Work item: 32 pairs = 4 consecutive rows x 8 consecutive columns, pair
+// index p = 4*jj + ii, which is also the order of one channel's 32 values in
+// x (128 contiguous bytes).  256 threads = 4 waves (one per SIMD), persistent
 // over the work items; the next item's x and z are prefetched into registers
-// while the current one is processed.
-//  - x: thread (pair p = tid % 64, channel group tid / 64) holds 16 channels;
+// while the current one is processed.  Two work-groups share each compute
+// unit and run out of step with each other, so the matrix-core phase of one
+// overlaps the LayerNorm phases (short dependent chains of vector, LDS and
+// cross-lane instructions) of the other on the same SIMD.
+//  - x: thread (pair p = tid % 32, channel group tid / 32) holds 16 channels;
 //    output LayerNorm statistics are combined over the 8 groups in LDS.
 //  - z is re-read (16 lanes per pair, 16-lane DPP reductions) and
 //    re-normalised for the gate.
@@ -17,8 +20,8 @@
 //    mode each is split into hi + lo bf16 terms (hi = bf16(v),
 //    lo = bf16(v - hi)) and multiplied by the bf16 weights twice, so the
 //    products keep fp32-level accuracy.
-//  - Wave w computes output channels 32*(w%4) .. +31 of both the projection
-//    and the gate for pairs 32*(w/4) .. +31, so the final product is formed in
+//  - Wave w computes output channels 32*w .. +31 of both the projection
+//    and the gate for the item's 32 pairs, so the final product is formed in
 //    registers and stored from there, 16 bytes (4 channels) per lane.  bf16
 //    weight fragments stay in registers for the whole pass.
 #include "common.hpp"
@@ -28,10 +31,12 @@ namespace trimul {
 
 namespace {
 
-constexpr int kPairs = 64;
-constexpr int kRows = 4, kCols = 16;  // work-item shape
-constexpr int kThreads = 512;
-constexpr int kXPer = kC / 8;         // x channels per thread
+constexpr int kPairs = 32;
+constexpr int kRows = 4, kCols = 8;   // work-item shape
+constexpr int kThreads = 256;
+constexpr int kGroups = kThreads / kPairs;   // x channel groups (8)
+constexpr int kXPer = kC / kGroups;          // x channels per thread (16)
+static_assert(kRows * kCols == kPairs && kThreads == 64 * 4, "one wave per SIMD");
 
 template <typename T>
 struct ZUnit;
@@ -64,8 +69,8 @@ struct ZUnit<float> {
   }
 };
 
-// LDS operand planes: bf16 mode keeps hi and lo planes [64][128] bf16 each;
-// fp32 mode keeps one plane [64][128] fp32.  Rows are 256 / 512 bytes, units
+// LDS operand planes: bf16 mode keeps hi and lo planes [32][128] bf16 each;
+// fp32 mode keeps one plane [32][128] fp32.  Rows are 256 / 512 bytes, units
 // of 8 channels XOR-swizzled with period 16.
 template <typename T>
 struct Operand;
@@ -132,14 +137,14 @@ struct Operand<float> {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k3_epilogue(K3Args p) {
   constexpr int E = sizeof(T);
   constexpr bool kWeightsInRegs = (E == 2);
   using Op = Operand<T>;
   constexpr int kOpBytes = Op::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char n_ops[kOpBytes];   // normalised x
   __shared__ __attribute__((aligned(16))) unsigned char z_ops[kOpBytes];   // normalised z
-  __shared__ __attribute__((aligned(8))) float2 part[8][kPairs];          // per-group (mean, M2)
+  __shared__ __attribute__((aligned(8))) float2 part[kGroups][kPairs];    // per-group (mean, M2)
   __shared__ __attribute__((aligned(4))) uint8_t mask_lds[kPairs];
 
   const int tid = threadIdx.x;
@@ -149,21 +154,21 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   const int64_t tiles_per_blk = (p.n_cols + kCols - 1) / kCols;
   const int64_t n_tiles = rows4 * tiles_per_blk;
 
-  // x channels of this thread: xc0 .. xc0+15 of pair q = lane
-  const int q = lane;
-  const int xc0 = kXPer * wave;
+  // x channels of this thread: xc0 .. xc0+15 of pair q
+  const int q = tid % kPairs;
+  const int grp = tid / kPairs;
+  const int xc0 = kXPer * grp;
   float gx[kXPer], bx[kXPer];
 #pragma unroll
   for (int c = 0; c < kXPer; ++c) { gx[c] = p.ln_out_w[xc0 + c]; bx[c] = p.ln_out_b[xc0 + c]; }
-  // z units of this thread: pairs 32*s + tid/16, channel group tid & 15
+  // z units of this thread: pairs 16*s + tid/16, channel group tid & 15
   const int cg = tid & 15;
   float gz[8], bz[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { gz[i] = p.ln_in_w[cg * 8 + i]; bz[i] = p.ln_in_b[cg * 8 + i]; }
 
-  // matrix-core rows (output channels) and pair half of this wave
-  const int o0 = 32 * (wave & 3);
-  const int ph = 32 * (wave >> 2);
+  // matrix-core rows (output channels) of this wave
+  const int o0 = 32 * wave;
   const T *const Wo = static_cast<const T *>(p.w_out_proj);
   const T *const Wg = static_cast<const T *>(p.w_out_gate);
   auto wptr = [&](const T *W, int ks) -> const T * {
@@ -190,18 +195,26 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
     const int64_t cc = col < p.n_cols ? col : p.n_cols - 1;
     return (p.row_off + rr) * p.n + p.col_off + cc;
   };
-  auto load_item = [&](int64_t tile) {
-    const int64_t blk = tile / tiles_per_blk;
-    const int64_t s0 = (tile % tiles_per_blk) * kCols;
-    // x: the item is one 4 x 16 block of the x layout (x_offset): 128
-    // channels x 64 pairs, contiguous, pair q at 4*jj + ii of each channel
+  // position of a work item: row block (4 rows) and first column
+  struct Pos {
+    int64_t blk, s0;
+  };
+  auto advance = [&](Pos &ps) {
+    ps.s0 += kCols;
+    if (ps.s0 >= p.n_cols) { ps.s0 = 0; ++ps.blk; }
+  };
+  auto load_item = [&](const Pos &ps) {
+    const int64_t blk = ps.blk, s0 = ps.s0;
+    // x: the item is one half (8 columns) of a 4 x 16 block of the x layout
+    // (x_offset): 128 channels x 32 pairs, 128 contiguous bytes per channel,
+    // pair q at 4*jj + ii
     const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
 #pragma unroll
     for (int c = 0; c < kXPer; ++c) xv[c] = xp[c * 64];
     bool valid;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int64_t idx = pair_index(blk, s0, 32 * s + (tid >> 4), valid);
+      const int64_t idx = pair_index(blk, s0, 16 * s + (tid >> 4), valid);
       zr[s].load(zbytes + (idx * kCz + cg * 8) * E);
     }
     mbyte = p.mask[pair_index(blk, s0, q, valid)];
@@ -209,21 +222,24 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
   };
 
   // Each work-group takes a contiguous range of work items, so consecutive
-  // items read consecutive 32 KB blocks of x and neighbouring columns of z.
+  // items read consecutive 16 KB half-blocks of x and neighbouring columns
+  // of z.
   const int64_t per_wg = (n_tiles + gridDim.x - 1) / gridDim.x;
   const int64_t tile_begin = blockIdx.x * per_wg;
   const int64_t tile_end = tile_begin + per_wg < n_tiles ? tile_begin + per_wg : n_tiles;
   int64_t tile = tile_begin;
-  if (tile < tile_end) load_item(tile);
+  Pos cur{tile_begin / tiles_per_blk, (tile_begin % tiles_per_blk) * kCols};
+  Pos nxt = cur;
+  advance(nxt);
+  if (tile < tile_end) load_item(cur);
 
   // Two barriers per item: (1) per-group LayerNorm partials written,
   // (2) normalised operands written.  The partials of the next item are
   // written after (2), when every wave has read the current ones; the
   // operands of the next item after its (1), when every wave has finished
   // this item's products.
-  for (; tile < tile_end; ++tile) {
-    const int64_t blk = tile / tiles_per_blk;
-    const int64_t s0 = (tile % tiles_per_blk) * kCols;
+  for (; tile < tile_end; ++tile, cur = nxt, advance(nxt)) {
+    const int64_t blk = cur.blk, s0 = cur.s0;
 
     // ---- output LayerNorm: exact per-thread partials over 16 channels,
     //      merged per pair across the 8 groups (Chan et al.'s pairwise
@@ -236,25 +252,25 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       float m2 = 0.f;
 #pragma unroll
       for (int c = 0; c < kXPer; ++c) { const float d = xv[c] - m; m2 += d * d; }
-      part[wave][q] = make_float2(m, m2);
-      if (wave == 0) mask_lds[q] = (mvalid && mbyte != 0) ? 1 : 0;
+      part[grp][q] = make_float2(m, m2);
+      if (grp == 0) mask_lds[q] = (mvalid && mbyte != 0) ? 1 : 0;
     }
     __syncthreads();   // (1)
     // mask of this lane's output pair, read before (2): the next item's
     // mask is written after it
-    const int pq = ph + (lane & 31);   // this lane's pair column
+    const int pq = lane & 31;   // this lane's pair column
     const bool keep = mask_lds[pq] != 0;
     {
-      float2 pg[8];
+      float2 pg[kGroups];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) pg[g] = part[g][q];
+      for (int g = 0; g < kGroups; ++g) pg[g] = part[g][q];
       float msum = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) msum += pg[g].x;
-      const float mean = msum * (1.0f / 8);
+      for (int g = 0; g < kGroups; ++g) msum += pg[g].x;
+      const float mean = msum * (1.0f / kGroups);
       float m2 = 0.f, dev = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) { m2 += pg[g].y; const float d = pg[g].x - mean; dev += d * d; }
+      for (int g = 0; g < kGroups; ++g) { m2 += pg[g].y; const float d = pg[g].x - mean; dev += d * d; }
       const float var = (m2 + kXPer * dev) * (1.0f / kC);
       const float rstd = rsqrt_f32(var + p.eps);
 #pragma unroll
@@ -281,12 +297,12 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
       const float zrs = rsqrt_f32(row_sum16(zq) * (1.0f / kCz) + p.eps);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * zrs * gz[i] + bz[i];
-      Op::put(z_ops, 32 * s + (tid >> 4), cg, f);
+      Op::put(z_ops, 16 * s + (tid >> 4), cg, f);
     }
     __syncthreads();   // (2)
 
     // ---- prefetch the next item ----------------------------------------------
-    if (tile + 1 < tile_end) load_item(tile + 1);
+    if (tile + 1 < tile_end) load_item(nxt);
 
     // ---- projections on the matrix cores ----------------------------------
     f32x16 ay, ag;
@@ -336,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void k3_epilogue(K3Args p) {
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s) {
   const int64_t n_tiles = ((a.n_rows + 3) / 4) * ((a.n_cols + kCols - 1) / kCols);
   if (n_tiles <= 0) return hipSuccess;
-  const int64_t cap = device_cu_count();
+  const int64_t cap = 2 * (int64_t)device_cu_count();   // two work-groups per compute unit
   const int64_t grid = n_tiles < cap ? n_tiles : cap;
   if (dtype == TRIMUL_BF16)
     hipLaunchKernelGGL(k3_epilogue<bf16_t>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
