@@ -83,11 +83,17 @@ __device__ __forceinline__ void lds_frag(Frag<T> &f, const unsigned char *row_ba
     dst[u] = *reinterpret_cast<const u32x4 *>(row_base + k2_swz(row, g * UPF + u) * 16);
 }
 
-// Number of 32-wide blocks of a wave's range that hold at least one valid
-// row, given `valid` rows from the start of the range; 0 .. cap.
-__device__ __forceinline__ int clamp_count(int valid, int cap) {
-  const int c = (valid + 31) / 32;
-  return valid <= 0 ? 0 : (c < cap ? c : cap);
+// Share of wave w (of `waves` along one side of the tile) in the 32-wide
+// blocks of a tile that hold at least one valid row, given `valid` rows from
+// the tile's start: a full tile gives every wave its own cap blocks; a tile
+// at the ragged edge spreads its valid blocks as evenly as possible, so the
+// busiest wave has as few as possible.  Returns the first block and the
+// count (0 .. cap).
+__device__ __forceinline__ void block_share(int valid, int cap, int waves, int w, int &first, int &count) {
+  const int nb = valid >= cap * waves * 32 ? cap * waves : (valid + 31) / 32;
+  const int per = nb / waves, extra = nb % waves;
+  count = per + (w < extra ? 1 : 0);
+  first = w * per + (w < extra ? w : extra);
 }
 
 // Rows of a tile covered by 32-row blocks that hold a valid row: valid rows
@@ -240,12 +246,15 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // to their consumers, so the LDS latency hides behind a whole step of
   // matrix-core work and the matrix core stays fed.
   //
-  // In a tile at the ragged edge of the output, 32-row (32-column) blocks of
-  // a wave that lie entirely past M (N) are padding: their fragment reads and
-  // products are skipped (wave-uniform counts), which makes the edge tiles of
-  // a ragged N cheaper; full tiles take a path without these checks.
-  const int mt_act = clamp_count((int)(p.M - m0) - wm * C::WM, C::MT);
-  const int nt_act = clamp_count((int)(p.N - n0) - wn * C::WN, C::NT);
+  // In a tile at the ragged edge of the output, 32-row (32-column) blocks
+  // that lie entirely past M (N) are padding: they are neither read nor
+  // multiplied, and the valid blocks are spread evenly over the waves of
+  // that side (wave-uniform counts), which makes the edge tiles of a ragged N
+  // cheaper; full tiles take a path without these checks.
+  int mb0, mt_act, nb0, nt_act;
+  block_share((int)(p.M - m0), C::MT, 2, wm, mb0, mt_act);
+  block_share((int)(p.N - n0), C::NT, 4, wn, nb0, nt_act);
+  const int row0 = 32 * mb0, col0 = 32 * nb0;   // this wave's first row / column in the tile
   const bool full = (mt_act == C::MT) && (nt_act == C::NT);
   auto compute = [&](int buf, auto whole) __attribute__((always_inline)) {
     constexpr bool kWhole = decltype(whole)::value;
@@ -254,14 +263,14 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
     Frag<T> af[C::MT], bfr[2][C::NT];
     const int g_lane = lane >> 5;   // which 8-element half of a 16-wide k step
     auto read_a = [&](int ks, int mt) __attribute__((always_inline)) {
-      const int row = wm * C::WM + mt * 32 + (lane & 31);
+      const int row = row0 + mt * 32 + (lane & 31);
       lds_frag(af[mt], sa + row * C::ROWB, row, 2 * ks + g_lane);
     };
     auto read_b = [&](int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) {
         if (!kWhole && nt >= nt_act) continue;
-        const int row = wn * C::WN + nt * 32 + (lane & 31);
+        const int row = col0 + nt * 32 + (lane & 31);
         lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, 2 * ks + g_lane);
       }
     };
@@ -305,17 +314,21 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // The four accumulator registers 4g..4g+3 of a lane are rows 4k..4k+3 of
   // one column: one 16-byte group of the x layout (x_offset); 16 lanes cover
   // the 16 columns of a 256-byte block row.  Rows of the last 4-row group
-  // past M hold products of padding rows and are ignored downstream.
+  // past M hold products of padding rows and are ignored downstream.  Only
+  // the wave's own blocks are written: in an edge tile the blocks past its
+  // count belong to the next wave (or to padding).
   const int M4 = (int)((p.M + 3) & ~int64_t(3));
   const int N = (int)p.N;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
+    if (mt >= mt_act) continue;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-      const int col = n0 + wn * C::WN + nt * 32 + (lane & 31);
+      if (nt >= nt_act) continue;
+      const int col = n0 + col0 + nt * 32 + (lane & 31);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int row4 = m0 + wm * C::WM + mt * 32 + acc_row(4 * g, lane);   // multiple of 4
+        const int row4 = m0 + row0 + mt * 32 + acc_row(4 * g, lane);   // multiple of 4
         if (row4 < M4 && col < N) {
           f32x4 *dst = reinterpret_cast<f32x4 *>(p.x + x_offset(row4, col, d, p.ldx));
           f32x4 v = {acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1], acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]};

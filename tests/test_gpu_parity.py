@@ -176,12 +176,15 @@ def test_operand_planes(dev, dtype, direction):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("m_rows,n_cols,klen", [(1, 1, 1), (40, 300, 77), (256, 256, 256), (300, 129, 515),
-                                                 (277, 300, 70), (21, 533, 64), (513, 31, 33)])
+                                                 (277, 300, 70), (21, 533, 64), (513, 31, 33), (150, 150, 70),
+                                                 (356, 533, 64), (100, 700, 40)])
 def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     """Contraction kernel fed the oracle's operands directly (uploaded, exact in
     the storage dtype) vs their float64 contraction.  The shapes include edge
     tiles with a few valid rows or columns past a 256 boundary (277 = 256 + 21,
-    533 = 512 + 21, 513) and single short tiles (21, 31)."""
+    533 = 512 + 21, 513), single short tiles (21, 31), and edge tiles whose
+    valid 32-blocks are spread unevenly over the waves (150, 356 = 256 + 100,
+    700 = 384 + 316)."""
     r = np.random.default_rng(m_rows * 7 + n_cols)
     ld = (klen + 63) // 64 * 64
     a = r.standard_normal((128, m_rows, klen))
