@@ -49,6 +49,13 @@ __device__ __forceinline__ float sigmoid_f32(float t) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * kLog2e));
 }
 
+// The same logistic function given u = -t log2 e instead of t: 1 / (1 + 2^u)
+// (u = +inf gives 0, u = -inf gives 1).  Callers that can fold the factor
+// -log2 e into an earlier scaling save the multiply.
+__device__ __forceinline__ float sigmoid_of_exp2_arg(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
+}
+
 __device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rsqf(v); }
 
 // Sum over aligned groups of G consecutive lanes (G a power of two <= 64);

@@ -82,9 +82,10 @@ struct Operand<bf16_t> {
     u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float h0 = bf16_to_f32(f32_to_bf16(f[2 * i]));
-      const float h1 = bf16_to_f32(f32_to_bf16(f[2 * i + 1]));
-      h[i] = pack_bf16x2(h0, h1);
+      // hi terms of both values from one packed rounding; unpacked exactly
+      h[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+      const float h0 = __uint_as_float(h[i] << 16);
+      const float h1 = __uint_as_float(h[i] & 0xffff0000u);
       l[i] = pack_bf16x2(f[2 * i] - h0, f[2 * i + 1] - h1);
     }
     const int off = q * ROWB + swz<16>(q, unit) * UNIT;
@@ -163,9 +164,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int c = 0; c < kXPer; ++c) { gx[c] = p.ln_out_w[xc0 + c]; bx[c] = p.ln_out_b[xc0 + c]; }
   // z units of this thread: pairs 16*s + tid/16, channel group tid & 15
   const int cg = tid & 15;
+  // The gate operand is kept as -log2(e) * LN_in(z): the products then give
+  // the argument of the base-2 exponential in the logistic function directly.
+  constexpr float kNegLog2e = -1.4426950408889634f;
   float gz[8], bz[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { gz[i] = p.ln_in_w[cg * 8 + i]; bz[i] = p.ln_in_b[cg * 8 + i]; }
+  for (int i = 0; i < 8; ++i) { gz[i] = p.ln_in_w[cg * 8 + i]; bz[i] = p.ln_in_b[cg * 8 + i] * kNegLog2e; }
 
   // matrix-core rows (output channels) of this wave
   const int o0 = 32 * wave;
@@ -203,6 +207,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     ps.s0 += kCols;
     if (ps.s0 >= p.n_cols) { ps.s0 = 0; ++ps.blk; }
   };
+  // pair offsets (relative to the item's first pair) of this thread's z
+  // units and mask byte, used for items that lie wholly inside the tile
+  int zoff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int pr = 16 * s + (tid >> 4);
+    zoff[s] = (pr & 3) * (int)p.n + (pr >> 2);
+  }
+  const int moff = (q & 3) * (int)p.n + (q >> 2);
   auto load_item = [&](const Pos &ps) {
     const int64_t blk = ps.blk, s0 = ps.s0;
     // x: the item is one half (8 columns) of a 4 x 16 block of the x layout
@@ -211,14 +224,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
 #pragma unroll
     for (int c = 0; c < kXPer; ++c) xv[c] = xp[c * 64];
-    bool valid;
+    if (blk * 4 + kRows <= p.n_rows && s0 + kCols <= p.n_cols) {
+      const int64_t base = (p.row_off + blk * 4) * p.n + p.col_off + s0;   // the item's first pair
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t idx = pair_index(blk, s0, 16 * s + (tid >> 4), valid);
-      zr[s].load(zbytes + (idx * kCz + cg * 8) * E);
+      for (int s = 0; s < 2; ++s) zr[s].load(zbytes + ((base + zoff[s]) * kCz + cg * 8) * E);
+      mbyte = p.mask[base + moff];
+      mvalid = true;
+    } else {
+      bool valid;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t idx = pair_index(blk, s0, 16 * s + (tid >> 4), valid);
+        zr[s].load(zbytes + (idx * kCz + cg * 8) * E);
+      }
+      mbyte = p.mask[pair_index(blk, s0, q, valid)];
+      mvalid = valid;
     }
-    mbyte = p.mask[pair_index(blk, s0, q, valid)];
-    mvalid = valid;
   };
 
   // Each work-group takes a contiguous range of work items, so consecutive
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       float zq = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { f[i] -= zm; zq += f[i] * f[i]; }
-      const float zrs = rsqrt_f32(row_sum16(zq) * (1.0f / kCz) + p.eps);
+      const float zrs = rsqrt_f32(row_sum16(zq) * (1.0f / kCz) + p.eps) * kNegLog2e;
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = f[i] * zrs * gz[i] + bz[i];
       Op::put(z_ops, 16 * s + (tid >> 4), cg, f);
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g4 + i;
-          const float gated = sigmoid_f32(ag[e]) * ay[e];
+          const float gated = sigmoid_of_exp2_arg(ag[e]) * ay[e];
           v[i] = keep ? gated : 0.f;
         }
         *reinterpret_cast<f32x4 *>(orow + acc_row(4 * g4, lane)) = v;
