@@ -65,15 +65,17 @@ struct ZUnit<float> {
 };
 
 // Write 8 normalised channels (one unit) into an LDS row, rounded to T.
-__device__ __forceinline__ void put_unit(unsigned char *dst, const float (&f)[8], bf16_t) {
+// Eight values of one LDS operand row, or zeros where `keep` is false (a
+// masked pair); the choice is made on the stored words.
+__device__ __forceinline__ void put_unit(unsigned char *dst, const float (&f)[8], bool keep, bf16_t) {
   u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  for (int i = 0; i < 4; ++i) w[i] = keep ? pack_bf16x2(f[2 * i], f[2 * i + 1]) : 0u;
   *reinterpret_cast<u32x4 *>(dst) = w;
 }
-__device__ __forceinline__ void put_unit(unsigned char *dst, const float (&f)[8], float) {
-  reinterpret_cast<f32x4 *>(dst)[0] = f32x4{f[0], f[1], f[2], f[3]};
-  reinterpret_cast<f32x4 *>(dst)[1] = f32x4{f[4], f[5], f[6], f[7]};
+__device__ __forceinline__ void put_unit(unsigned char *dst, const float (&f)[8], bool keep, float) {
+  reinterpret_cast<f32x4 *>(dst)[0] = keep ? f32x4{f[0], f[1], f[2], f[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+  reinterpret_cast<f32x4 *>(dst)[1] = keep ? f32x4{f[4], f[5], f[6], f[7]} : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Four consecutive plane elements of one channel.
@@ -181,15 +183,33 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
     const int64_t j = p.transposed ? p.row_base + rr : p.k_off + tt;
     return i * p.n + j;
   };
-  auto load_item = [&](Pos q) {
+  // pair offsets of this thread's two units from the item's first pair
+  // (consecutive plane columns are consecutive pairs, or pairs n apart when
+  // the plane is transposed); used for items that lie wholly in range
+  int64_t poff[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int pr = 32 * s + (tid >> 4);   // pair within the item
+  for (int s = 0; s < 2; ++s) poff[s] = (int64_t)(32 * s + (tid >> 4)) * (p.transposed ? p.n : 1);
+  auto load_item = [&](Pos q) {
+    if (q.r < p.n_rows && q.t0 + kPairs <= p.k_len) {
       bool valid;
-      const int64_t idx = pair_index(q.r, q.t0 + pr, valid);
-      raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
-      mbyte[s] = p.mask[idx];
-      mvalid[s] = valid;
+      const int64_t base = pair_index(q.r, q.t0, valid);   // wave-uniform
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t idx = base + poff[s];
+        raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
+        mbyte[s] = p.mask[idx];
+        mvalid[s] = true;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pr = 32 * s + (tid >> 4);   // pair within the item
+        bool valid;
+        const int64_t idx = pair_index(q.r, q.t0 + pr, valid);
+        raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
+        mbyte[s] = p.mask[idx];
+        mvalid[s] = valid;
+      }
     }
   };
 
@@ -211,9 +231,9 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       const float rstd = rsqrt_f32(row_sum16(sq) * (1.0f / kCz) + p.eps);
       const bool keep = mvalid[s] && mbyte[s] != 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = keep ? f[i] * rstd * g8[i] + b8[i] : 0.f;
+      for (int i = 0; i < 8; ++i) f[i] = f[i] * rstd * g8[i] + b8[i];
       const int pr = 32 * s + (tid >> 4);
-      put_unit(zh_lds[buf] + pr * ROWB + swz<16>(pr, cg) * UNIT, f, T{});
+      put_unit(zh_lds[buf] + pr * ROWB + swz<16>(pr, cg) * UNIT, f, keep, T{});
     }
   };
 
