@@ -29,7 +29,7 @@
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
-// tiles; inside a channel, tiles go in groups of kGroupM tile-rows so that the
+// tiles; inside a channel, tiles go in groups of group_m tile-rows so that the
 // concurrently running tiles of one XCD share operand panels in its L2.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -43,7 +43,6 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kLoadWaves = 4;   // waves that issue the operand loads (one per SIMD)
 constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -130,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // runs on XCD x = (b % slots) % 8; give that XCD the contiguous logical
   // tiles s*slots + x*(slots/8) + .., so each round works on ~one channel
   // (its operands stay in the shared last-level cache) and each XCD on a
-  // compact kGroupM x 8 block of it (operand panels shared in its L2).
+  // compact group_m x 8 block of it (operand panels shared in its L2).
   const int slots = p.slots;
   const int round = blockIdx.x / slots;
   const int pos = blockIdx.x - round * slots;
@@ -138,11 +137,12 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   if (logical >= total) return;
   const int d = logical / per_ch;
   const int t = logical - d * per_ch;
-  const int group = t / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int group_m = p.group_m;
+  const int group = t / (group_m * tiles_n);
+  const int first_m = group * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
   const int tm = first_m + (t % gm);
-  const int tn = (t % (kGroupM * tiles_n)) / gm;
+  const int tn = (t % (group_m * tiles_n)) / gm;
   const int m0 = tm * BM, n0 = tn * BN;
 
   // ---- direct-to-LDS loads --------------------------------------------
@@ -348,7 +348,11 @@ hipError_t launch_k2(K2Args a, int dtype, hipStream_t s) {
   const int64_t bm = (dtype == TRIMUL_BF16) ? 256 : 128;
   const int64_t bn = (dtype == TRIMUL_BF16) ? 384 : 128;
   for (int c = 0; c < a.n_chunks; ++c) a.ch[c].ktiles = (int32_t)((a.ch[c].k_len + bk - 1) / bk);
-  const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * kC;
+  const int64_t tiles_m = (a.M + bm - 1) / bm;
+  const int64_t tiles = tiles_m * ((a.N + bn - 1) / bn) * kC;
+  // Tile-row groups of 4..6 that divide the tile rows evenly (a short last
+  // group shares fewer operand panels), else 4.
+  a.group_m = (tiles_m % 4 == 0) ? 4 : (tiles_m % 5 == 0) ? 5 : (tiles_m % 6 == 0) ? 6 : 4;
   // resident work-groups: one per CU for bf16 (160 KB of LDS), two for fp32
   const int per_cu = (dtype == TRIMUL_BF16) ? 1 : 2;
   a.slots = (device_cu_count() * per_cu + kXcds - 1) / kXcds * kXcds;

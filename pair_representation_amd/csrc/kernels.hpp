@@ -44,7 +44,7 @@ struct K2Args {
   int32_t n_chunks;
   int32_t accumulate;     // 1: x += result, 0: x = result
   int32_t slots;          // work-groups resident at once (multiple of 8; set by the launcher)
-  int32_t pad_;
+  int32_t group_m;        // tile-rows per group of the tile order (set by the launcher)
   int64_t M, N;           // tile rows (a operand rows), tile cols (b operand rows)
   float *x;               // [c][round_up(M,4)/4][ldx][4] (4-row blocks), ldx = round_up(N,16)
   int64_t ldx;
