@@ -255,60 +255,103 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   block_share((int)(p.M - m0), C::MT, 2, wm, mb0, mt_act);
   block_share((int)(p.N - n0), C::NT, 4, wn, nb0, nt_act);
   const int row0 = 32 * mb0, col0 = 32 * nb0;   // this wave's first row / column in the tile
-  const bool full = (mt_act == C::MT) && (nt_act == C::NT);
-  auto compute = [&](int buf, auto whole) __attribute__((always_inline)) {
-    constexpr bool kWhole = decltype(whole)::value;
+  // The k-loop runs with compile-time block bounds MTA x NTA and, in the
+  // checked form, skips blocks past the wave's own counts with wave-uniform
+  // branches; see the dispatch after it.
+  auto compute = [&](int buf, auto mta, auto nta, auto checked) __attribute__((always_inline)) {
+    constexpr int MTA = decltype(mta)::value, NTA = decltype(nta)::value;
+    constexpr bool kChecked = decltype(checked)::value;
     const unsigned char *sa = lds + buf * C::STAGE;
     const unsigned char *sb = sa + BM * C::ROWB;
-    Frag<T> af[C::MT], bfr[2][C::NT];
+    // Wave tiles of up to 8 blocks keep two register sets of A and B
+    // fragments and read all of step ks+1 during step ks.  Larger ones (128 x
+    // 96) do not fit in 256 registers that way: their A fragments are
+    // single-buffered, each re-read for the next step right after the
+    // products of the current step that use it have been issued.
+    constexpr bool kRollA = C::MT * C::NT > 8;
+    Frag<T> af[kRollA ? 1 : 2][C::MT], bfr[2][C::NT];
     const int g_lane = lane >> 5;   // which 8-element half of a 16-wide k step
-    auto read_a = [&](int ks, int mt) __attribute__((always_inline)) {
+    auto read_a = [&](int ks, int slot, int mt) __attribute__((always_inline)) {
       const int row = row0 + mt * 32 + (lane & 31);
-      lds_frag(af[mt], sa + row * C::ROWB, row, 2 * ks + g_lane);
+      lds_frag(af[slot][mt], sa + row * C::ROWB, row, 2 * ks + g_lane);
     };
     auto read_b = [&](int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) {
-        if (!kWhole && nt >= nt_act) continue;
+      for (int nt = 0; nt < NTA; ++nt) {
+        if (kChecked && nt >= nt_act) continue;
         const int row = col0 + nt * 32 + (lane & 31);
         lds_frag(bfr[slot][nt], sb + row * C::ROWB, row, 2 * ks + g_lane);
       }
     };
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      if (kWhole || mt < mt_act) read_a(0, mt);
+    for (int mt = 0; mt < MTA; ++mt)
+      if (!kChecked || mt < mt_act) read_a(0, 0, mt);
     read_b(0, 0);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < C::KS) read_b(ks + 1, cur ^ 1);
+      const int aslot = kRollA ? 0 : cur;
+      if (ks + 1 < C::KS) {
+        read_b(ks + 1, cur ^ 1);
+        if (!kRollA) {
+#pragma unroll
+          for (int mt = 0; mt < MTA; ++mt)
+            if (!kChecked || mt < mt_act) read_a(ks + 1, aslot ^ 1, mt);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        if (!kWhole && mt >= mt_act) continue;
+      for (int mt = 0; mt < MTA; ++mt) {
+        if (kChecked && mt >= mt_act) continue;
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-          if (kWhole || nt < nt_act) mma(acc[mt][nt], af[mt], bfr[cur][nt]);
-        if (ks + 1 < C::KS) read_a(ks + 1, mt);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int nt = 0; nt < NTA; ++nt)
+          if (!kChecked || nt < nt_act) mma(acc[mt][nt], af[aslot][mt], bfr[cur][nt]);
+        if (kRollA && ks + 1 < C::KS) read_a(ks + 1, 0, mt);
+        if (kRollA) __builtin_amdgcn_sched_barrier(0);
       }
+      if (!kRollA) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto k_loop = [&](auto whole) __attribute__((always_inline)) {
+  auto k_loop = [&](auto mta, auto nta, auto checked) __attribute__((always_inline)) {
     for (int it = 0; it + 1 < total_kt; ++it) {
       const int buf = it & 1;
       issue_loads(ci, kt, buf ^ 1);
       advance();
-      compute(buf, whole);
+      compute(buf, mta, nta, checked);
       wait_vm0();
       __syncthreads();
     }
-    if (total_kt > 0) compute((total_kt - 1) & 1, whole);
+    if (total_kt > 0) compute((total_kt - 1) & 1, mta, nta, checked);
   };
-  if (full)
-    k_loop(std::true_type{});
-  else
-    k_loop(std::false_type{});
+  // Dispatch.  Every wave runs exactly one k-loop, so its barriers pair
+  // with the other waves'.
+  //  - 128 x 96 wave tiles (384-wide tiles): full waves run the check-free
+  //    loop, the others the checked loop, which multiplies exactly their own
+  //    blocks (measured fastest at N = 3605, where edge waves have 1-2 blocks).
+  //  - smaller wave tiles: straight-line loops with row blocks 1, 2 or MT and
+  //    column blocks 1 or NT, a count in between rounded up (the extra blocks
+  //    lie inside the tile, multiply stale LDS rows and are never written);
+  //    the checked loop is slow when edge waves keep most of their blocks.
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using IM = std::integral_constant<int, C::MT>;
+  using IN = std::integral_constant<int, C::NT>;
+  if constexpr (C::MT * C::NT > 8) {
+    if (mt_act == C::MT && nt_act == C::NT) k_loop(IM{}, IN{}, F{});
+    else k_loop(IM{}, IN{}, Tr{});
+  } else {
+    auto k_loop_n = [&](auto mta) __attribute__((always_inline)) {
+      if (nt_act == 1) k_loop(mta, I1{}, F{});
+      else k_loop(mta, IN{}, F{});
+    };
+    if (mt_act == 0 || nt_act == 0) k_loop(I0{}, I0{}, F{});   // loads and barriers only
+    else if (mt_act == 1) k_loop_n(I1{});
+    else if (mt_act == 2) k_loop_n(std::conditional_t<(C::MT > 2), I2, IM>{});
+    else k_loop_n(IM{});
+  }
 
   // ---- write / accumulate x -------------------------------------------
   // The four accumulator registers 4g..4g+3 of a lane are rows 4k..4k+3 of
@@ -342,23 +385,34 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 
 }  // namespace
 
+// bf16 tile width: 384 columns (wave tile 128 x 96, fewer operand bytes and
+// LDS fragment reads per product) unless its last tile column would pad
+// clearly more of N than 256-wide tiles do (the padding tiles still pay the
+// full load stream of the k-loop).
+static int64_t bf16_tile_cols(int64_t n) {
+  const int64_t pad384 = (n + 383) / 384 * 384 - n, pad256 = (n + 255) / 256 * 256 - n;
+  return (pad384 - pad256) * 100 > 3 * n ? 256 : 384;
+}
+
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   const int64_t bk = (dtype == TRIMUL_BF16) ? 64 : 32;
   const int64_t bm = (dtype == TRIMUL_BF16) ? 256 : 128;
-  const int64_t bn = (dtype == TRIMUL_BF16) ? 384 : 128;
+  const int64_t bn = (dtype == TRIMUL_BF16) ? bf16_tile_cols(a.N) : 128;
   for (int c = 0; c < a.n_chunks; ++c) a.ch[c].ktiles = (int32_t)((a.ch[c].k_len + bk - 1) / bk);
   const int64_t tiles_m = (a.M + bm - 1) / bm;
   const int64_t tiles = tiles_m * ((a.N + bn - 1) / bn) * kC;
   // Tile-row groups of 4..6 that divide the tile rows evenly (a short last
   // group shares fewer operand panels), else 4.
   a.group_m = (tiles_m % 4 == 0) ? 4 : (tiles_m % 5 == 0) ? 5 : (tiles_m % 6 == 0) ? 6 : 4;
-  // resident work-groups: one per CU for bf16 (160 KB of LDS), two for fp32
+  // resident work-groups: one per CU for bf16 (128 or 160 KB of LDS), two for fp32
   const int per_cu = (dtype == TRIMUL_BF16) ? 1 : 2;
   a.slots = (device_cu_count() * per_cu + kXcds - 1) / kXcds * kXcds;
   const int64_t grid = (tiles + a.slots - 1) / a.slots * a.slots;
-  if (dtype == TRIMUL_BF16)
+  if (dtype == TRIMUL_BF16 && bn == 384)
     hipLaunchKernelGGL((k2_contract<bf16_t, 256, 384, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else if (dtype == TRIMUL_BF16)
+    hipLaunchKernelGGL((k2_contract<bf16_t, 256, 256, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((k2_contract<float, 128, 128, 32>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
