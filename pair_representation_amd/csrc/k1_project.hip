@@ -300,20 +300,35 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   __syncthreads();
 
   // One barrier per item.  The matrix-core products of this item, the
-  // LayerNorm of the next one, the loads of the one after and the gates of
-  // pair tile 0 are mutually independent straight-line code, so the compiler
-  // interleaves vector work with the matrix-core instructions.  Waves with no
-  // output run the products on unused weights and skip the stores.
+  // LayerNorm of the next one (after the last item: a stand-in nobody reads)
+  // and the loads of the one after are mutually independent.  The two waves
+  // of a SIMD (w and w + 4) take them in opposite orders between the same
+  // barriers, so one wave's products overlap the other's LayerNorm instead of
+  // both waiting for the one matrix core at once.  Waves with no output run
+  // the products on unused weights and skip the stores.
   for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
     const int buf = (int)((tile - tile_begin) & 1);
-    products(buf, 0);
-    layer_norm(buf ^ 1);   // after the last item: a stand-in nobody reads
-    products(buf, 1);
-    gate(0);
-    ahead = next_pos(ahead);
-    load_item(ahead);
-    gate(1);
-    store_out(cur);
+    // (each order is one straight-line block, gates and stores included, so
+    // the compiler can interleave all of it)
+    if (wave < 4) {
+      products(buf, 0);
+      products(buf, 1);
+      layer_norm(buf ^ 1);
+      ahead = next_pos(ahead);
+      load_item(ahead);
+      gate(0);
+      gate(1);
+      store_out(cur);
+    } else {
+      layer_norm(buf ^ 1);
+      ahead = next_pos(ahead);
+      load_item(ahead);
+      products(buf, 0);
+      products(buf, 1);
+      gate(0);
+      gate(1);
+      store_out(cur);
+    }
     cur = next_pos(cur);
     __syncthreads();
   }
