@@ -21,7 +21,8 @@ source of the tiled (sub-block) evaluation in ``tile_partial``.
 Modules
 -------
 trimul_ref   vectorised float64 definition, Q-mode (bf16 contraction operands),
-             blockwise and sampled evaluation, tile partial sums.
+             blockwise and sampled evaluation, tile partial sums, and the
+             gradients of the contraction step with respect to its operands.
 bruteforce   per-element scalar loops of the same definition, for tiny inputs.
 
 Parity status: every function here is pinned by the CPU tests in
@@ -34,6 +35,7 @@ from .trimul_ref import (  # noqa: F401
     WEIGHT_KEYS,
     array_getters,
     contract_rows,
+    contract_rows_vjp,
     bf16_round,
     contract,
     finish,

@@ -81,3 +81,23 @@ def trimul_loops(z, mask, w, direction, eps=1e-5):
             m = 1.0 if mask[i][j] else 0.0
             out[i][j] = [m * _sig(g[e]) * y[e] for e in range(len(y))]
     return out
+
+
+def contract_vjp_loops(a_rows, b_rows, dx):
+    """Scalar loops for the gradients of L = sum dx[i][j][d] * x[i][j][d],
+    x[i][j][d] = sum_k a_rows[i][k][d] * b_rows[j][k][d]: every term of L
+    that contains a_rows[i][k][d] is dx[i][j][d] * a_rows[i][k][d] *
+    b_rows[j][k][d] for some j, so its derivative collects those b values
+    (and symmetrically for b_rows).  Nested lists in, nested lists out."""
+    Mi, K, c = len(a_rows), len(a_rows[0]), len(a_rows[0][0])
+    Mj = len(b_rows)
+    da = [[[0.0] * c for _ in range(K)] for _ in range(Mi)]
+    db = [[[0.0] * c for _ in range(K)] for _ in range(Mj)]
+    for i in range(Mi):
+        for j in range(Mj):
+            for k in range(K):
+                for d in range(c):
+                    g = dx[i][j][d]
+                    da[i][k][d] += g * b_rows[j][k][d]
+                    db[j][k][d] += g * a_rows[i][k][d]
+    return da, db

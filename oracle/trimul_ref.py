@@ -134,6 +134,27 @@ def contract_rows(a_rows, b_rows):
     return np.moveaxis(X, 0, 2)
 
 
+def contract_rows_vjp(a_rows, b_rows, dx):
+    """Gradients of the scalar L = sum_{i,j,d} dx[i, j, d] * x[i, j, d] with
+    x = contract_rows(a_rows, b_rows), with respect to both operands:
+
+        da[i, k, d] = sum_j dx[i, j, d] * b_rows[j, k, d]
+        db[j, k, d] = sum_i dx[i, j, d] * a_rows[i, k, d]
+
+    (per channel d: dA_d = dX_d B_d and dB_d = dX_d^T A_d), done by
+    ``numpy.matmul`` on channel-major copies.  ``dx`` is [Mi, Mj, c]; the
+    results have the shapes of ``a_rows`` and ``b_rows``.  This is the backward
+    of the contraction step of the layer, which page 1 (section "Pra quem e")
+    expects to be wrapped in custom autograd functions for training.
+    """
+    A = np.ascontiguousarray(np.moveaxis(_f64(a_rows), 2, 0))       # [c, Mi, K]
+    B = np.ascontiguousarray(np.moveaxis(_f64(b_rows), 2, 0))       # [c, Mj, K]
+    DX = np.ascontiguousarray(np.moveaxis(_f64(dx), 2, 0))          # [c, Mi, Mj]
+    dA = np.matmul(DX, B)                                           # [c, Mi, K]
+    dB = np.matmul(np.swapaxes(DX, 1, 2), A)                        # [c, Mj, K]
+    return np.moveaxis(dA, 0, 2), np.moveaxis(dB, 0, 2)
+
+
 def contract(a, b, direction):
     """The k-contraction over the full pair grid ([N, N, c] each).
 

@@ -395,3 +395,60 @@ def test_golden_fixture():
     m = np.array(g["mask"], np.uint8)
     for d in ("outgoing", "incoming"):
         assert rel(oracle.trimul(z, m, w, d), np.array(g["out_" + d])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# gradients of the contraction step (backward pass): pinned by the
+# bilinearity identity, finite differences, scalar loops and one-hot inputs
+# ---------------------------------------------------------------------------
+
+def _vjp_case(seed, mi=5, mj=4, k=6, c=3):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((mi, k, c)), r.standard_normal((mj, k, c)), r.standard_normal((mi, mj, c)))
+
+
+def test_contract_vjp_bilinearity():
+    # x is linear in each operand, so <dx, x(a, b)> = <da, a> = <db, b>
+    a, b, dx = _vjp_case(1)
+    da, db = oracle.contract_rows_vjp(a, b, dx)
+    L = float(np.sum(dx * oracle.contract_rows(a, b)))
+    assert abs(float(np.sum(da * a)) - L) <= 1e-12 * abs(L) + 1e-12
+    assert abs(float(np.sum(db * b)) - L) <= 1e-12 * abs(L) + 1e-12
+    assert da.shape == a.shape and db.shape == b.shape
+
+
+def test_contract_vjp_finite_differences():
+    # L(a + h v) - L(a - h v) = 2 h <da, v> exactly for a linear L (up to rounding)
+    a, b, dx = _vjp_case(2)
+    da, db = oracle.contract_rows_vjp(a, b, dx)
+    r = np.random.default_rng(3)
+    L = lambda a_, b_: float(np.sum(dx * oracle.contract_rows(a_, b_)))
+    for _ in range(3):
+        v = r.standard_normal(a.shape)
+        h = 1e-3
+        fd = (L(a + h * v, b) - L(a - h * v, b)) / (2 * h)
+        assert abs(fd - float(np.sum(da * v))) < 1e-9 * (1 + abs(fd))
+        u = r.standard_normal(b.shape)
+        fd = (L(a, b + h * u) - L(a, b - h * u)) / (2 * h)
+        assert abs(fd - float(np.sum(db * u))) < 1e-9 * (1 + abs(fd))
+
+
+def test_contract_vjp_matches_loops():
+    a, b, dx = _vjp_case(4, mi=3, mj=4, k=5, c=2)
+    da, db = oracle.contract_rows_vjp(a, b, dx)
+    la, lb = bruteforce.contract_vjp_loops(a.tolist(), b.tolist(), dx.tolist())
+    assert np.max(np.abs(da - np.array(la))) < 1e-12
+    assert np.max(np.abs(db - np.array(lb))) < 1e-12
+
+
+def test_contract_vjp_one_hot():
+    # dx = e_(i0, j0, d0): da is row j0 of b in channel d0, placed at row i0;
+    # db is row i0 of a, placed at row j0
+    a, b, _ = _vjp_case(5)
+    dx = np.zeros((a.shape[0], b.shape[0], a.shape[2]))
+    i0, j0, d0 = 3, 1, 2
+    dx[i0, j0, d0] = 1.0
+    da, db = oracle.contract_rows_vjp(a, b, dx)
+    ea = np.zeros_like(a); ea[i0, :, d0] = b[j0, :, d0]
+    eb = np.zeros_like(b); eb[j0, :, d0] = a[i0, :, d0]
+    assert np.array_equal(da, ea) and np.array_equal(db, eb)
