@@ -174,6 +174,91 @@ def bench_tile(work, args, dev):
             "config": {"workload": work.name, "n": work.n, "tile": t}, "directions": res}
 
 
+def bench_backward(work, args, dev):
+    """Backward of the contraction step (trimul_tile_backward) on the whole
+    N x N grid as one tile and one chunk: dA = dX B and dB = dX^T A per
+    channel from the workload's outgoing operands (K1 on the seeded z) and a
+    seeded gradient dX, timed with HIP events on the launch stream around the
+    entry point (its relayout kernels and two contractions).  The rate counts
+    the N^2 pair gradients of x per call; the roofline is the two contractions'
+    4 N^3 c flop over the whole call (a lower bound for the contraction
+    kernels; the per-kernel split is in the committed rocprofv3 summary)."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    n = work.n
+    log(f"[bench] generating {work.name} (N={n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    kp = (n + 63) // 64 * 64
+    a_pl, b_pl = pra.tile_operands(w, pra.OUTGOING, z, mask, 0, n, 0, n, 0, n, kp)
+    del z
+    g = torch.Generator(device=dev).manual_seed(12345)
+    dx = torch.randn(pra.xacc_shape(n, n), generator=g, device=dev)
+    chunks = [(0, n, a_pl, b_pl)]
+    da = [pra.new_xacc(n, n, dev)]
+    db = [pra.new_xacc(n, n, dev)]
+    ws = torch.empty(pra.tile_backward_workspace_bytes(w, n, n, chunks), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        pra.tile_backward(w, n, n, chunks, dx, da, db, ws)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} backward calls")
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        pra.tile_backward(w, n, n, chunks, dx, da, db, ws)
+        e[1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    t = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e-3
+    flops = 4.0 * n * n * n * C
+    rec = {
+        "metric": "TriMul contraction-backward pair-gradients/s (dA, dB) at N=3605, c=128 bf16 (1 GPU)",
+        "value": n * n / t, "unit": "pair-gradients/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": work.dtype, "data": "synthetic (workload operands from the seeded z; seeded N(0,1) dX)",
+        "config": {"workload": work.name, "n": n, "part": "contraction backward, one tile, one chunk"},
+        "roofline": {"bound": "mfma", "kernel": "trimul_tile_backward (relayouts + two contractions)",
+                     "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_per_launch": f"4*N^3*c = {flops:.4e} flop", "avg_launch_ms": t * 1e3},
+        "cpu_baseline": None,
+    }
+    del da, db, ws, dx, a_pl, b_pl
+    torch.cuda.empty_cache()
+    if args.cpu_rows > 0:
+        rec["cpu_baseline"] = cpu_baseline_backward(work, args.cpu_rows)
+    return rec
+
+
+def cpu_baseline_backward(work, block_rows, block_k=128):
+    """The oracle's contraction gradients (numpy float64 matmul on all host
+    cores) on a block: dA for block_rows rows of a seeded dX against block_k
+    columns of a full-height b (2 * block_rows * N * block_k * c flop),
+    extrapolated to both gradients of the whole grid (4 N^3 c flop)."""
+    import numpy as np
+
+    import oracle
+
+    n = work.n
+    r = np.random.default_rng(5)
+    b = r.standard_normal((n, block_k, C))
+    dx = r.standard_normal((block_rows, n, C))
+    a_blk = np.zeros((block_rows, block_k, C))
+    t0 = time.perf_counter()
+    oracle.contract_rows_vjp(a_blk, b, dx)
+    t_blk = time.perf_counter() - t0
+    scale = (n / block_rows) * (n / block_k) * 2.0
+    t_full = t_blk * scale
+    return {"value": n * n / t_full, "unit": "pair-gradients/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"oracle.contract_rows_vjp: {block_rows} rows of dX against {block_k} k-columns of a "
+                      f"{n}-row b ({t_blk:.2f}s), extrapolated x{scale:.0f} to both gradients of the "
+                      f"{n}x{n} grid ({t_full:.0f}s)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,8 +266,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
-                    help="copy: run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "backward"],
+                    help="copy: run a plain device copy of known size (HBM counter calibration); "
+                         "backward: the contraction step's gradients (trimul_tile_backward)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -207,6 +293,9 @@ def main():
                           "launches": 3}), flush=True)
         return
     work = wl.WORKLOADS[args.workload]
+    if args.mode == "backward":
+        print(json.dumps(bench_backward(work, args, dev)), flush=True)
+        return
     if work.tile:
         print(json.dumps(bench_tile(work, args, dev)), flush=True)
         return

@@ -191,6 +191,37 @@ trimul_status_t trimul_tile(const trimul_weights_t *w, int64_t n, int64_t row_of
                             uint32_t flags, float *x_acc, const void *z, const uint8_t *mask,
                             float *out_tile, void *stream);
 
+/* Backward of the k-contraction of one tile: the gradients a training step
+ * needs from trimul_tile's contraction (page 1, section "Pra quem e": the
+ * layer is trained through custom autograd functions; sections "O problema
+ * dos workarounds atuais" and "A pegadinha": training and fine-tuning need
+ * the large crops the tiling makes possible).  Per channel d the contraction
+ * is x = A B^T over the stored operands, so given
+ *   dx = dL/dx of the tile (fp32, the x_acc layout of trimul_tile, rows
+ *        n_rows, columns n_cols; entries past them are ignored)
+ * it writes, for every chunk c (host array; the operands as passed to
+ * trimul_tile, only a, b, k_len and ld are used),
+ *   da_out[c][d][r][t] = sum_s dx[d][r][s] * b_c[d][s][t]     r < n_rows
+ *   db_out[c][d][s][t] = sum_r dx[d][r][s] * a_c[d][r][t]     s < n_cols
+ * for t < k_len: the gradients with respect to the stored operands (for
+ * incoming, stored transposed, da_out[c][d][r][t] is the gradient of
+ * a_(k_off+t, row_off+r)).  da_out and db_out are host arrays of n_chunks
+ * device pointers, fp32 in the x_acc layout with rows r (s) and columns t:
+ * trimul_tile_xacc_bytes(w, n_rows, k_len) and (w, n_cols, k_len) bytes each,
+ * fully overwritten.  In bf16 mode dx is rounded to bf16 (nearest-even) for
+ * the matrix-core products, as the forward rounds a and b; accumulation is
+ * fp32.  workspace >= trimul_tile_backward_workspace_bytes(...) bytes,
+ * 256-byte aligned (dx and its transpose as operand buffers, one chunk's
+ * transposed operands); contents on entry are ignored. */
+size_t trimul_tile_backward_workspace_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols,
+                                            const trimul_kchunk_t *chunks /* (host) */, int32_t n_chunks);
+
+trimul_status_t trimul_tile_backward(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols,
+                                     const trimul_kchunk_t *chunks /* (host) */, int32_t n_chunks,
+                                     const float *dx, float *const *da_out /* (host) */,
+                                     float *const *db_out /* (host) */, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *trimul_status_string(trimul_status_t s);
 

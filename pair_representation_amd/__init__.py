@@ -87,6 +87,11 @@ def lib():
         L.trimul_tile.argtypes = [W, i64, i64, i64, i64, i64, ctypes.POINTER(KChunk), i32, u32, vp, vp,
                                   vp, vp, vp]
         L.trimul_tile.restype = ctypes.c_int
+        L.trimul_tile_backward_workspace_bytes.argtypes = [W, i64, i64, ctypes.POINTER(KChunk), i32]
+        L.trimul_tile_backward_workspace_bytes.restype = sz
+        L.trimul_tile_backward.argtypes = [W, i64, i64, ctypes.POINTER(KChunk), i32, vp,
+                                           ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+        L.trimul_tile_backward.restype = ctypes.c_int
         L.trimul_status_string.argtypes = [ctypes.c_int]
         L.trimul_status_string.restype = ctypes.c_char_p
         L.trimul_last_error.argtypes = []
@@ -288,3 +293,50 @@ def tile(w: Weights, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, 
     _check(lib().trimul_tile(w.ref, n, row_off, n_rows, col_off, n_cols, arr, len(chunks), flags,
                              _ptr(x_acc), _ptr(z), _ptr(mask), _ptr(out_tile), _stream()))
     return out_tile
+
+
+def _chunk_array(w: Weights, n_rows, n_cols, chunks):
+    arr = (KChunk * max(1, len(chunks)))()
+    for i, (k_off, k_len, a, b) in enumerate(chunks):
+        _need(a, f"chunk {i} a", w.torch_dtype)
+        _need(b, f"chunk {i} b", w.torch_dtype)
+        ld = a.shape[1] * 64 if a.dim() == 5 else -1
+        if tuple(a.shape) != operand_shape(n_rows, ld):
+            raise ValueError(f"chunk {i} a must have shape operand_shape({n_rows}, ld)")
+        if tuple(b.shape) != operand_shape(n_cols, ld):
+            raise ValueError(f"chunk {i} b must have shape operand_shape({n_cols}, ld) with a's ld")
+        arr[i] = KChunk(k_off, k_len, ld, a.data_ptr(), b.data_ptr())
+    return arr
+
+
+def tile_backward_workspace_bytes(w: Weights, n_rows, n_cols, chunks) -> int:
+    return int(lib().trimul_tile_backward_workspace_bytes(w.ref, n_rows, n_cols,
+                                                          _chunk_array(w, n_rows, n_cols, chunks), len(chunks)))
+
+
+def tile_backward(w: Weights, n_rows, n_cols, chunks, dx, da=None, db=None, workspace=None):
+    """Gradients of a tile's contraction with respect to the chunk operands.
+
+    ``chunks`` is a list of (k_off, k_len, a, b) as for tile(); ``dx`` is the
+    gradient of the tile's contraction result in the accumulator layout
+    (xacc_shape(n_rows, n_cols), fp32).  Returns (da, db): per chunk, fp32
+    accumulator-layout tensors of shapes xacc_shape(n_rows, k_len) and
+    xacc_shape(n_cols, k_len) (allocated if not given)."""
+    _need(dx, "dx", torch.float32, xacc_shape(n_rows, n_cols))
+    arr = _chunk_array(w, n_rows, n_cols, chunks)
+    if da is None:
+        da = [new_xacc(n_rows, k_len, dx.device) for (_, k_len, _, _) in chunks]
+    if db is None:
+        db = [new_xacc(n_cols, k_len, dx.device) for (_, k_len, _, _) in chunks]
+    for i, (_, k_len, _, _) in enumerate(chunks):
+        _need(da[i], f"da[{i}]", torch.float32, xacc_shape(n_rows, k_len))
+        _need(db[i], f"db[{i}]", torch.float32, xacc_shape(n_cols, k_len))
+    need = int(lib().trimul_tile_backward_workspace_bytes(w.ref, n_rows, n_cols, arr, len(chunks)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dx.device)
+    _need(workspace, "workspace", torch.uint8)
+    da_ptrs = (ctypes.c_void_p * len(chunks))(*[t.data_ptr() for t in da])
+    db_ptrs = (ctypes.c_void_p * len(chunks))(*[t.data_ptr() for t in db])
+    _check(lib().trimul_tile_backward(w.ref, n_rows, n_cols, arr, len(chunks), _ptr(dx), da_ptrs, db_ptrs,
+                                      _ptr(workspace), workspace.numel(), _stream()))
+    return da, db

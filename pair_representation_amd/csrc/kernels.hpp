@@ -5,6 +5,8 @@
 //                        streaming k-chunks in the given order
 //   K3 (k3_epilogue.hip) output LayerNorm + output projection + output gate
 //                        + pair mask, fp32 output
+//   KB (kb_relayout.hip) layout copies and transposes for the contraction's
+//                        gradients
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,11 +66,27 @@ struct K3Args {
   const void *w_out_gate;  // [c_z][c_z]
 };
 
+// KB (kb_relayout.hip): 64 x 64 tile copies between the x layout and the
+// operand layout, and operand-plane transposes, for the contraction's
+// gradients (dA = dX B, dB = dX^T A).
+struct RelayoutArgs {
+  const float *x;         // fp32 source in the x layout (from_x), ldx its padded columns
+  int64_t ldx;
+  const void *src;        // operand-layout source of the element type (otherwise)
+  int64_t ld_src;         // >= round_up(cols, 64)
+  int64_t rows, cols;     // valid rows / columns of the source matrix
+  void *p;                // [c][rows][ld_p] same orientation (operand layout) or null
+  int64_t ld_p;           // >= round_up(cols, 64); columns cols .. round_up(cols, 64) get zeros
+  void *q;                // [c][cols][ld_q] transpose (operand layout) or null
+  int64_t ld_q;           // >= round_up(rows, 64); columns rows .. round_up(rows, 64) get zeros
+};
+
 // Each launcher checks the launch with hipGetLastError.  dtype is
 // TRIMUL_F32 or TRIMUL_BF16.
 hipError_t launch_k1(const K1Args &a, int dtype, hipStream_t s);
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s);
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s);
+hipError_t launch_relayout(const RelayoutArgs &a, bool from_x, int dtype, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -128,6 +128,52 @@ trimul::K3Args k3_args(const trimul_weights_t *w, const float *x, int64_t ldx, c
   return a;
 }
 
+// Workspace of trimul_tile_backward: dx as an operand buffer (rows n_rows,
+// row length ld_j = round_up(n_cols, 64)) and transposed (rows n_cols, row
+// length ld_i = round_up(n_rows, 64)), then one chunk's transposed a (rows
+// k_len, length ld_i) and transposed b (rows k_len, length ld_j), sized for the
+// longest chunk.
+struct BackwardLayout {
+  int64_t ld_i, ld_j, kmax;
+  size_t p_off, pt_off, at_off, bt_off, total;
+};
+
+BackwardLayout backward_layout(int32_t dtype, int64_t n_rows, int64_t n_cols, const trimul_kchunk_t *chunks,
+                               int32_t n_chunks) {
+  BackwardLayout L;
+  L.ld_i = round_up(n_rows, kKTile);
+  L.ld_j = round_up(n_cols, kKTile);
+  L.kmax = 1;
+  for (int i = 0; i < n_chunks; ++i) L.kmax = std::max<int64_t>(L.kmax, chunks[i].k_len);
+  L.p_off = 0;
+  L.pt_off = L.p_off + align256(operand_bytes(n_rows, L.ld_j, dtype));
+  L.at_off = L.pt_off + align256(operand_bytes(n_cols, L.ld_i, dtype));
+  L.bt_off = L.at_off + align256(operand_bytes(L.kmax, L.ld_i, dtype));
+  L.total = L.bt_off + align256(operand_bytes(L.kmax, L.ld_j, dtype));
+  return L;
+}
+
+trimul_status_t check_backward(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols,
+                               const trimul_kchunk_t *chunks, int32_t n_chunks) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (n_rows < 1 || n_rows > kMaxN || n_cols < 1 || n_cols > kMaxN)
+    return fail(TRIMUL_ERR_INVALID_ARG, "tile %lld x %lld outside [1, %lld]^2", (long long)n_rows, (long long)n_cols,
+                (long long)kMaxN);
+  if (n_chunks < 1 || n_chunks > TRIMUL_MAX_CHUNKS)
+    return fail(TRIMUL_ERR_INVALID_ARG, "n_chunks=%d outside [1, %d]", n_chunks, TRIMUL_MAX_CHUNKS);
+  if (!chunks) return fail(TRIMUL_ERR_INVALID_ARG, "chunks is NULL");
+  for (int i = 0; i < n_chunks; ++i) {
+    const trimul_kchunk_t &c = chunks[i];
+    if (c.k_len < 1 || c.k_len > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: k_len=%lld", i, (long long)c.k_len);
+    if (c.ld < c.k_len || c.ld % kKTile != 0)
+      return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: ld=%lld must be a multiple of 64 and >= k_len", i, (long long)c.ld);
+    if (!c.a || !c.b) return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: NULL operand", i);
+    if (!aligned(c.a, 16) || !aligned(c.b, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "chunk %d: operands must be 16-byte aligned", i);
+  }
+  return TRIMUL_OK;
+}
+
 trimul_status_t hip_fail(hipError_t e, const char *what) {
   return fail(TRIMUL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -364,6 +410,93 @@ trimul_status_t trimul_tile(const trimul_weights_t *w, int64_t n, int64_t row_of
     trimul::K3Args k3 = k3_args(w, x_acc, x_ld(n_cols), z, mask, n, row_off, n_rows, col_off, n_cols, out_tile);
     e = trimul::launch_k3(k3, w->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
+  }
+  return ok();
+}
+
+size_t trimul_tile_backward_workspace_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols,
+                                            const trimul_kchunk_t *chunks, int32_t n_chunks) {
+  if (check_backward(w, n_rows, n_cols, chunks, n_chunks) != TRIMUL_OK) return 0;
+  return backward_layout(w->dtype, n_rows, n_cols, chunks, n_chunks).total;
+}
+
+trimul_status_t trimul_tile_backward(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols,
+                                     const trimul_kchunk_t *chunks, int32_t n_chunks, const float *dx,
+                                     float *const *da_out, float *const *db_out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  trimul_status_t st = check_backward(w, n_rows, n_cols, chunks, n_chunks);
+  if (st != TRIMUL_OK) return st;
+  if (!dx) return fail(TRIMUL_ERR_INVALID_ARG, "dx is NULL");
+  if (!aligned(dx, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "dx must be 16-byte aligned");
+  if (!da_out || !db_out) return fail(TRIMUL_ERR_INVALID_ARG, "da_out and db_out must be host arrays");
+  for (int i = 0; i < n_chunks; ++i) {
+    if (!da_out[i] || !db_out[i]) return fail(TRIMUL_ERR_INVALID_ARG, "chunk %d: NULL gradient output", i);
+    if (!aligned(da_out[i], 16) || !aligned(db_out[i], 16))
+      return fail(TRIMUL_ERR_ALIGNMENT, "chunk %d: gradient outputs must be 16-byte aligned", i);
+  }
+  const BackwardLayout L = backward_layout(w->dtype, n_rows, n_cols, chunks, n_chunks);
+  if (!workspace) return fail(TRIMUL_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  void *P = ws + L.p_off, *Pt = ws + L.pt_off, *At = ws + L.at_off, *Bt = ws + L.bt_off;
+  hipError_t e;
+  // dx -> operand buffers P = dx (rows r, columns s) and Pt = dx^T
+  trimul::RelayoutArgs r{};
+  r.x = dx;
+  r.ldx = x_ld(n_cols);
+  r.rows = n_rows;
+  r.cols = n_cols;
+  r.p = P;
+  r.ld_p = L.ld_j;
+  r.q = Pt;
+  r.ld_q = L.ld_i;
+  e = trimul::launch_relayout(r, true, w->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "relayout kernel launch");
+  for (int c = 0; c < n_chunks; ++c) {
+    const trimul_kchunk_t &ch = chunks[c];
+    // a^T: rows t < k_len, columns r < n_rows; b^T: rows t, columns s < n_cols
+    trimul::RelayoutArgs ta{};
+    ta.src = ch.a;
+    ta.ld_src = ch.ld;
+    ta.rows = n_rows;
+    ta.cols = ch.k_len;
+    ta.q = At;
+    ta.ld_q = L.ld_i;
+    e = trimul::launch_relayout(ta, false, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "transpose kernel launch");
+    trimul::RelayoutArgs tb = ta;
+    tb.src = ch.b;
+    tb.rows = n_cols;
+    tb.q = Bt;
+    tb.ld_q = L.ld_j;
+    e = trimul::launch_relayout(tb, false, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "transpose kernel launch");
+    // da[r][t] = sum_s P[r][s] Bt[t][s];  db[s][t] = sum_r Pt[s][r] At[t][r]
+    trimul::K2Args k2{};
+    k2.n_chunks = 1;
+    k2.accumulate = 0;
+    k2.ch[0].a = P;
+    k2.ch[0].b = Bt;
+    k2.ch[0].ld = L.ld_j;
+    k2.ch[0].k_len = n_cols;
+    k2.M = n_rows;
+    k2.N = ch.k_len;
+    k2.x = da_out[c];
+    k2.ldx = x_ld(ch.k_len);
+    e = trimul::launch_k2(k2, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "contraction kernel launch (da)");
+    k2.ch[0].a = Pt;
+    k2.ch[0].b = At;
+    k2.ch[0].ld = L.ld_i;
+    k2.ch[0].k_len = n_rows;
+    k2.M = n_cols;
+    k2.x = db_out[c];
+    e = trimul::launch_k2(k2, w->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "contraction kernel launch (db)");
   }
   return ok();
 }

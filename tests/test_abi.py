@@ -189,6 +189,62 @@ def test_tile_validation():
     assert "cover" in pra.lib().trimul_last_error().decode() or True
 
 
+def call_bwd(chunks=None, n_rows=50, n_cols=40, dx=FAKE, da=FAKE + 0x3000000, db=FAKE + 0x4000000,
+             ws=FAKE + 0x8000000, ws_bytes=None, w=None, n_chunks=None, null_out=None):
+    L = pra.lib()
+    w = weights() if w is None else w
+    if chunks is None:
+        chunks = [(0, 100, 128)]
+    arr = (pra.KChunk * max(1, len(chunks)))()
+    for i, (ko, kl, ld) in enumerate(chunks):
+        arr[i] = pra.KChunk(ko, kl, ld, FAKE + 0x1000000 * (i + 1), FAKE + 0x1000000 * (i + 40))
+    nc = len(chunks) if n_chunks is None else n_chunks
+    das = (ctypes.c_void_p * max(1, len(chunks)))(*([da] * max(1, len(chunks))))
+    dbs = (ctypes.c_void_p * max(1, len(chunks)))(*([db] * max(1, len(chunks))))
+    if null_out == "da":
+        das[0] = None
+    if ws_bytes is None:
+        ws_bytes = L.trimul_tile_backward_workspace_bytes(ctypes.byref(w), n_rows, n_cols, arr, nc)
+    return L.trimul_tile_backward(ctypes.byref(w), n_rows, n_cols, arr, nc, dx, das, dbs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("dtype,elt", [(pra.BF16, 2), (pra.F32, 4)])
+def test_backward_workspace_closed_form(dtype, elt):
+    L = pra.lib()
+    w = weights(dtype)
+    a256 = lambda v: round_up(v, 256)
+    arr = (pra.KChunk * 2)(pra.KChunk(0, 1250, 1280, FAKE, FAKE), pra.KChunk(1250, 700, 704, FAKE, FAKE))
+    n_rows, n_cols, kmax = 5000, 300, 1250
+    li, lj = round_up(n_rows, 64), round_up(n_cols, 64)
+    want = (a256(128 * round_up(n_rows, 256) * lj * elt) + a256(128 * round_up(n_cols, 256) * li * elt)
+            + a256(128 * round_up(kmax, 256) * li * elt) + a256(128 * round_up(kmax, 256) * lj * elt))
+    assert L.trimul_tile_backward_workspace_bytes(ctypes.byref(w), n_rows, n_cols, arr, 2) == want
+    assert L.trimul_tile_backward_workspace_bytes(ctypes.byref(w), 0, n_cols, arr, 2) == 0
+    assert L.trimul_tile_backward_workspace_bytes(ctypes.byref(w), n_rows, n_cols, arr, 0) == 0
+
+
+def test_backward_validation():
+    assert call_bwd(w=weights(c=64)) == pra.ERR_UNSUPPORTED
+    assert call_bwd(n_rows=0) == pra.ERR_INVALID_ARG
+    assert call_bwd(n_cols=70000) == pra.ERR_INVALID_ARG
+    assert call_bwd(chunks=[]) == pra.ERR_INVALID_ARG
+    assert call_bwd(n_chunks=33, chunks=[(0, 100, 128)] * 33) == pra.ERR_INVALID_ARG
+    assert call_bwd(chunks=[(0, 0, 64)]) == pra.ERR_INVALID_ARG
+    assert call_bwd(chunks=[(0, 100, 96)]) == pra.ERR_INVALID_ARG        # ld % 64
+    assert call_bwd(chunks=[(0, 100, 64)]) == pra.ERR_INVALID_ARG        # ld < k_len
+    assert call_bwd(dx=None) == pra.ERR_INVALID_ARG
+    assert call_bwd(dx=FAKE + 4) == pra.ERR_ALIGNMENT
+    assert call_bwd(null_out="da") == pra.ERR_INVALID_ARG
+    assert call_bwd(db=FAKE + 8) == pra.ERR_ALIGNMENT
+    assert call_bwd(ws=None) == pra.ERR_INVALID_ARG
+    assert call_bwd(ws=FAKE + 0x10) == pra.ERR_ALIGNMENT
+    L = pra.lib()
+    arr = (pra.KChunk * 1)(pra.KChunk(0, 100, 128, FAKE, FAKE))
+    need = L.trimul_tile_backward_workspace_bytes(ctypes.byref(weights()), 50, 40, arr, 1)
+    assert call_bwd(ws_bytes=need - 1) == pra.ERR_WORKSPACE_TOO_SMALL
+    assert str(need) in L.trimul_last_error().decode()
+
+
 def test_status_strings():
     L = pra.lib()
     for s in range(6):
