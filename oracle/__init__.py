@@ -22,7 +22,7 @@ Modules
 -------
 trimul_ref   vectorised float64 definition, Q-mode (bf16 contraction operands),
              blockwise and sampled evaluation, tile partial sums, and the
-             gradients of the contraction step with respect to its operands.
+             gradients of the contraction step and of the epilogue.
 bruteforce   per-element scalar loops of the same definition, for tiny inputs.
 
 Parity status: every function here is pinned by the CPU tests in
@@ -39,6 +39,7 @@ from .trimul_ref import (  # noqa: F401
     bf16_round,
     contract,
     finish,
+    finish_vjp,
     layer_norm,
     project,
     sigmoid,

@@ -181,6 +181,68 @@ def finish(x, z, mask, w, eps=LN_EPS):
     return m * g * y
 
 
+def _ln_parts(v, eps):
+    """Normalised v (before the affine map) and 1 / sqrt(var + eps), biased var."""
+    v = _f64(v)
+    mu = v.mean(axis=-1, keepdims=True)
+    d = v - mu
+    r = 1.0 / np.sqrt((d * d).mean(axis=-1, keepdims=True) + eps)
+    return d * r, r
+
+
+def _ln_vjp(g_hat, v_hat, r):
+    """Gradient with respect to the LayerNorm input v, given the gradient g_hat
+    with respect to the normalised v_hat = (v - mean) * r (biased variance):
+    r * (g_hat - mean(g_hat) - v_hat * mean(g_hat * v_hat))."""
+    return r * (g_hat - g_hat.mean(axis=-1, keepdims=True)
+                - v_hat * (g_hat * v_hat).mean(axis=-1, keepdims=True))
+
+
+def finish_vjp(x, z, mask, w, dout, eps=LN_EPS):
+    """Gradients of L = sum(dout * finish(x, z, mask, w)), the backward of the
+    epilogue (the layer's output LayerNorm, output projection, output gate and
+    mask), with respect to x, to z through the gate's input LayerNorm (the
+    gate path's share of dL/dz; the a/b projections add the rest), and to the
+    parameters the epilogue uses.  Returns a dict with keys x, z, w_out_proj,
+    w_out_gate, ln_out_w, ln_out_b, ln_in_w, ln_in_b (the last two: the gate
+    path's share).  float64, following the forward's steps backwards:
+
+        n = LN(x) = nh*g_o + b_o,  y = W_o n,  zh = LN(z) = zhh*g_i + b_i,
+        t = W_g zh,  s = sigmoid(t),  out = m * s * y
+        dy = m*s*dout,  dt = m*y*dout * s*(1 - s)
+        dW_o = sum dy (x) n,  dn = W_o^T dy,  dg_o = sum dn*nh,  db_o = sum dn
+        dx = LN backward of dn*g_o
+        dW_g = sum dt (x) zh,  dzh = W_g^T dt,  dg_i = sum dzh*zhh,  db_i = sum dzh
+        dz = LN backward of dzh*g_i
+    (sums over all pairs).  Page 1 (section "Pra quem e") expects the layer to
+    be trained through custom autograd functions; this is the epilogue's part.
+    """
+    x, z, g = _f64(x), _f64(z), _f64(dout)
+    m = (_f64(mask) != 0).astype(np.float64)[..., None]
+    nh, rx = _ln_parts(x, eps)
+    n = nh * _f64(w["ln_out_w"]) + _f64(w["ln_out_b"])
+    y = _lin(n, w["w_out_proj"])
+    zhh, rz = _ln_parts(z, eps)
+    zh = zhh * _f64(w["ln_in_w"]) + _f64(w["ln_in_b"])
+    s = sigmoid(_lin(zh, w["w_out_gate"]))
+    dy = m * s * g
+    dt = m * y * g * s * (1.0 - s)
+    c, cz = n.shape[-1], zh.shape[-1]
+    dy2, n2, dt2, zh2 = dy.reshape(-1, cz), n.reshape(-1, c), dt.reshape(-1, cz), zh.reshape(-1, cz)
+    dn = dy @ _f64(w["w_out_proj"])
+    dzh = dt @ _f64(w["w_out_gate"])
+    return {
+        "x": _ln_vjp(dn * _f64(w["ln_out_w"]), nh, rx),
+        "z": _ln_vjp(dzh * _f64(w["ln_in_w"]), zhh, rz),
+        "w_out_proj": dy2.T @ n2,
+        "w_out_gate": dt2.T @ zh2,
+        "ln_out_w": (dn * nh).reshape(-1, c).sum(axis=0),
+        "ln_out_b": dn.reshape(-1, c).sum(axis=0),
+        "ln_in_w": (dzh * zhh).reshape(-1, cz).sum(axis=0),
+        "ln_in_b": dzh.reshape(-1, cz).sum(axis=0),
+    }
+
+
 def trimul(z, mask, w, direction, quant=False, eps=LN_EPS, return_x=False):
     """Whole update on a full [N, N, c_z] pair tensor; returns [N, N, c_z]."""
     a, b = project(z, mask, w, quant, eps)

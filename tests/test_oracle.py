@@ -452,3 +452,63 @@ def test_contract_vjp_one_hot():
     ea = np.zeros_like(a); ea[i0, :, d0] = b[j0, :, d0]
     eb = np.zeros_like(b); eb[j0, :, d0] = a[i0, :, d0]
     assert np.array_equal(da, ea) and np.array_equal(db, eb)
+
+
+# ---------------------------------------------------------------------------
+# gradients of the epilogue: pinned by central finite differences of
+# oracle.finish, closed-form special cases and the LayerNorm shift invariance
+# ---------------------------------------------------------------------------
+
+def _epi_case(seed, p=6, c=5, cz=7, keep=0.7):
+    r = np.random.default_rng(seed)
+    w = {"ln_out_w": 1 + 0.3 * r.standard_normal(c), "ln_out_b": 0.2 * r.standard_normal(c),
+         "ln_in_w": 1 + 0.3 * r.standard_normal(cz), "ln_in_b": 0.2 * r.standard_normal(cz),
+         "w_out_proj": r.standard_normal((cz, c)) / np.sqrt(c), "w_out_gate": r.standard_normal((cz, cz)) / np.sqrt(cz)}
+    x = r.standard_normal((p, c)) * 2 + 0.5
+    z = r.standard_normal((p, cz))
+    m = (r.random(p) < keep).astype(np.uint8)
+    m[0] = 1
+    dout = r.standard_normal((p, cz))
+    return x, z, m, w, dout
+
+
+def test_finish_vjp_finite_differences():
+    x, z, m, w, dout = _epi_case(21)
+    g = oracle.finish_vjp(x, z, m, w, dout)
+    L = lambda x_, z_, w_: float(np.sum(dout * oracle.finish(x_, z_, m, w_)))
+    r = np.random.default_rng(22)
+    h = 1e-5
+    for name in ("x", "z"):
+        v = r.standard_normal(x.shape if name == "x" else z.shape)
+        if name == "x":
+            fd = (L(x + h * v, z, w) - L(x - h * v, z, w)) / (2 * h)
+        else:
+            fd = (L(x, z + h * v, w) - L(x, z - h * v, w)) / (2 * h)
+        assert abs(fd - float(np.sum(g[name] * v))) < 1e-7 * (1 + abs(fd)), name
+    for key in ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b"):
+        v = r.standard_normal(np.shape(w[key]))
+        wp = dict(w); wp[key] = w[key] + h * v
+        wm = dict(w); wm[key] = w[key] - h * v
+        fd = (L(x, z, wp) - L(x, z, wm)) / (2 * h)
+        assert abs(fd - float(np.sum(g[key] * v))) < 1e-7 * (1 + abs(fd)), key
+
+
+def test_finish_vjp_special_cases():
+    x, z, m, w, dout = _epi_case(23)
+    # LayerNorm removes a common shift, so each pair's input gradients sum to 0
+    g = oracle.finish_vjp(x, z, m, w, dout)
+    assert np.max(np.abs(g["x"].sum(axis=-1))) < 1e-12
+    assert np.max(np.abs(g["z"].sum(axis=-1))) < 1e-12
+    # all pairs masked: the output is identically 0, so is every gradient
+    g0 = oracle.finish_vjp(x, z, np.zeros_like(m), w, dout)
+    assert all(np.max(np.abs(v)) == 0 for v in g0.values())
+    # gamma_out = 0: the output does not depend on x
+    w1 = dict(w); w1["ln_out_w"] = np.zeros_like(w["ln_out_w"])
+    assert np.max(np.abs(oracle.finish_vjp(x, z, m, w1, dout)["x"])) == 0
+    # W_g = 0: sigmoid = 1/2, so d/dW_o = sum 0.5 m dout (x) n and dz = 0
+    w2 = dict(w); w2["w_out_gate"] = np.zeros_like(w["w_out_gate"])
+    g2 = oracle.finish_vjp(x, z, m, w2, dout)
+    n = oracle.layer_norm(x, w["ln_out_w"], w["ln_out_b"])
+    want = (0.5 * m[:, None] * dout).T @ n
+    assert np.max(np.abs(g2["w_out_proj"] - want)) < 1e-12
+    assert np.max(np.abs(g2["z"])) == 0
