@@ -8,8 +8,10 @@
 // 2 x 4 layout, each wave a (BM/2) x (BN/4) block of 32 x 32 matrix-core
 // accumulators; the two waves of a SIMD hide each other's LDS and barrier
 // latency.  bf16: 256 x 384 x 64 (wave tile 128 x 96: 192 accumulator
-// registers, two 80 KB LDS stages); fp32: 128 x 128 x 32.  The k-loop walks the chunks in the order given (a ring's
-// delivery order) and, inside each chunk, BK-wide k-tiles.
+// registers, two 80 KB LDS stages) or, when 384-wide tiles would pad much
+// more of N, 256 x 256 x 64 (chosen per launch); fp32: 128 x 128 x 32.  The
+// k-loop walks the chunks in the order given (a ring's delivery order) and,
+// inside each chunk, BK-wide k-tiles.
 //
 // Operand staging: buffer loads that write LDS directly (no register
 // staging), two LDS stages, one barrier per k-tile: the loads of k-tile t+1
@@ -18,14 +20,16 @@
 // at consecutive addresses), so the XOR swizzle of 16-byte units inside a row
 // (unit u of row r stored at u ^ ((r / 2) % 8)) is applied on the global
 // side: a lane fetches the logical unit that belongs in its LDS slot.  In the
-// operand layout (see operand_offset) a k-tile of one channel is a single
-// contiguous 32 KB run; rows past the operand's end are padding rows of the
-// last 256-row block and only feed output rows/columns that are never stored
-// (in edge tiles, whole 32-row blocks of padding are skipped).  k-fragments
-// are read from LDS ahead of the matrix-core instructions that consume them:
-// B fragments a whole 16-wide k step ahead (two register sets), A fragments
-// one at a time, each re-read for the next step as soon as the products of
-// the current step that use it have been issued (one register set).
+// operand layout (see operand_offset) a k-tile of one channel is a contiguous
+// 32 KB run per 256-row block; rows past the operand's end are padding rows
+// of the last block and only feed output rows/columns that are never stored
+// (in edge tiles, whole 32-row blocks of padding are skipped and the valid
+// blocks are spread evenly over the waves).  k-fragments are read from LDS
+// ahead of the matrix-core instructions that consume them: a whole 16-wide k
+// step ahead (two register sets) for wave tiles of up to 8 blocks; for
+// 128 x 96 wave tiles the A fragments are single-buffered, each re-read for
+// the next step as soon as the products of the current step that use it have
+// been issued.
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the linear block
 // id is remapped so that each XCD receives a contiguous range of logical
