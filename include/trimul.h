@@ -222,6 +222,54 @@ trimul_status_t trimul_tile_backward(const trimul_weights_t *w, int64_t n_rows, 
                                      float *const *db_out /* (host) */, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Parameter gradients of the epilogue, fp32, each fully overwritten. */
+typedef struct {
+  float *w_out_proj;           /* [c_z][c]   dL/dW_out_proj                      */
+  float *w_out_gate;           /* [c_z][c_z] dL/dW_out_gate                      */
+  float *ln_out_w;             /* [c]        dL/d(output LayerNorm gamma)        */
+  float *ln_out_b;             /* [c]        dL/d(output LayerNorm beta)         */
+  float *ln_in_w;              /* [c_z]      the output gate's share of
+                                              dL/d(input LayerNorm gamma)        */
+  float *ln_in_b;              /* [c_z]      the same for beta                   */
+} trimul_epilogue_grads_t;
+
+/* Backward of the epilogue of one tile (the step trimul_tile runs with
+ * TRIMUL_TILE_LAST): the rest of the training step around
+ * trimul_tile_backward (page 1, section "Pra quem e": the layer is trained
+ * through custom autograd functions).  With n = LN(x; ln_out), y = W_out_proj n,
+ * zh = LN(z; ln_in), s = sigmoid(W_out_gate zh) and out = m s y, given
+ *   dout = dL/dout_tile ([n_rows][n_cols][c_z] fp32, the layout of out_tile)
+ * and the forward's inputs (x_acc as trimul_tile left it, the global z and
+ * mask) it writes
+ *   dx     = dL/dx in the x_acc layout (rows n_rows, columns n_cols; entries
+ *            past them are not written): the dx of trimul_tile_backward.
+ *            dx may be x_acc itself (each pair's x is read before its dx is
+ *            written).
+ *   dz     = [n_rows][n_cols][c_z] fp32: the output gate's share of
+ *            dL/dz_(row_off+r, col_off+s) (through ln_in and W_out_gate; the
+ *            a/b projections contribute the rest)
+ *   grads  = sums over the tile's pairs (masked pairs contribute nothing; a
+ *            layer split into tiles sums the tiles' results)
+ * Masked pairs get dx = dz = 0.  The weight-matrix gradients are formed as
+ * dW_out_proj = G diag(ln_out_w) + S ln_out_b^T with G = sum dy LN0(x)^T and
+ * S = sum dy (dy = m s dout, LN0 = LayerNorm before its affine map), the
+ * LayerNorm parameter gradients from the same sums (sum over o of
+ * W_out_proj[o][k] G[o][k], W_out_proj^T S), and the gate's from the same
+ * construction.  Precision: as the forward epilogue (bf16 mode: the stored
+ * bf16 matrices, every other operand of a matrix-core product split into two
+ * bf16 terms; fp32 mode: fp32 products), fp32 accumulation, a fixed summation
+ * order.  workspace >= trimul_epilogue_backward_workspace_bytes(w) bytes,
+ * 256-byte aligned (transposed matrices, per-work-group partial sums);
+ * contents on entry are ignored. */
+size_t trimul_epilogue_backward_workspace_bytes(const trimul_weights_t *w);
+
+trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, int64_t row_off,
+                                         int64_t n_rows, int64_t col_off, int64_t n_cols,
+                                         const float *x_acc, const void *z, const uint8_t *mask,
+                                         const float *dout, float *dx, float *dz,
+                                         const trimul_epilogue_grads_t *grads /* (host) */,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *trimul_status_string(trimul_status_t s);
 

@@ -12,6 +12,10 @@ Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     tile_operand_bytes(w, rows, ld)
     tile_operands(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, ...)
     tile(w, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z, mask, out_tile)
+    tile_backward_workspace_bytes(w, n_rows, n_cols, chunks)
+    tile_backward(w, n_rows, n_cols, chunks, dx, ...)
+    epilogue_backward_workspace_bytes(w)
+    epilogue_backward(w, n, row_off, n_rows, col_off, n_cols, x_acc, z, mask, dout, ...)
 """
 
 from __future__ import annotations
@@ -58,6 +62,14 @@ class KChunk(ctypes.Structure):
                 ("a", ctypes.c_void_p), ("b", ctypes.c_void_p)]
 
 
+class _EpilogueGrads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b")]
+
+
+EPILOGUE_GRAD_SHAPES = {"w_out_proj": (C_Z, C), "w_out_gate": (C_Z, C_Z), "ln_out_w": (C,), "ln_out_b": (C,),
+                        "ln_in_w": (C_Z,), "ln_in_b": (C_Z,)}
+
 _lib = None
 
 
@@ -92,6 +104,11 @@ def lib():
         L.trimul_tile_backward.argtypes = [W, i64, i64, ctypes.POINTER(KChunk), i32, vp,
                                            ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
         L.trimul_tile_backward.restype = ctypes.c_int
+        L.trimul_epilogue_backward_workspace_bytes.argtypes = [W]
+        L.trimul_epilogue_backward_workspace_bytes.restype = sz
+        L.trimul_epilogue_backward.argtypes = [W, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                               ctypes.POINTER(_EpilogueGrads), vp, sz, vp]
+        L.trimul_epilogue_backward.restype = ctypes.c_int
         L.trimul_status_string.argtypes = [ctypes.c_int]
         L.trimul_status_string.restype = ctypes.c_char_p
         L.trimul_last_error.argtypes = []
@@ -340,3 +357,44 @@ def tile_backward(w: Weights, n_rows, n_cols, chunks, dx, da=None, db=None, work
     _check(lib().trimul_tile_backward(w.ref, n_rows, n_cols, arr, len(chunks), _ptr(dx), da_ptrs, db_ptrs,
                                       _ptr(workspace), workspace.numel(), _stream()))
     return da, db
+
+
+def epilogue_backward_workspace_bytes(w: Weights) -> int:
+    return int(lib().trimul_epilogue_backward_workspace_bytes(w.ref))
+
+
+def epilogue_backward(w: Weights, n, row_off, n_rows, col_off, n_cols, x_acc, z, mask, dout, dx=None, dz=None,
+                      grads=None, workspace=None):
+    """Backward of a tile's epilogue.
+
+    ``x_acc`` is the tile's contraction result (accumulator layout, as
+    tile() leaves it), ``z``/``mask`` the global [n, n] tensors and ``dout``
+    the gradient of the tile's output [n_rows, n_cols, 128] fp32.  Returns
+    (dx, dz, grads): dx in the accumulator layout (may be passed as x_acc
+    itself), dz [n_rows, n_cols, 128] (the output gate's share of dL/dz) and a
+    dict of fp32 parameter gradients keyed as EPILOGUE_GRAD_SHAPES (allocated
+    when not given)."""
+    _need(x_acc, "x_acc", torch.float32, xacc_shape(n_rows, n_cols))
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    _need(dout, "dout", torch.float32, (n_rows, n_cols, C_Z))
+    dev = x_acc.device
+    if dx is None:
+        dx = new_xacc(n_rows, n_cols, dev)
+    if dz is None:
+        dz = torch.empty((n_rows, n_cols, C_Z), dtype=torch.float32, device=dev)
+    _need(dx, "dx", torch.float32, xacc_shape(n_rows, n_cols))
+    _need(dz, "dz", torch.float32, (n_rows, n_cols, C_Z))
+    if grads is None:
+        grads = {k: torch.empty(shp, dtype=torch.float32, device=dev) for k, shp in EPILOGUE_GRAD_SHAPES.items()}
+    for k, shp in EPILOGUE_GRAD_SHAPES.items():
+        _need(grads[k], f"grads[{k!r}]", torch.float32, shp)
+    g = _EpilogueGrads(*[grads[k].data_ptr() for k in EPILOGUE_GRAD_SHAPES])
+    need = epilogue_backward_workspace_bytes(w)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib().trimul_epilogue_backward(w.ref, n, row_off, n_rows, col_off, n_cols, _ptr(x_acc), _ptr(z),
+                                          _ptr(mask), _ptr(dout), _ptr(dx), _ptr(dz), ctypes.byref(g),
+                                          _ptr(workspace), workspace.numel(), _stream()))
+    return dx, dz, grads

@@ -7,6 +7,8 @@
 //                        + pair mask, fp32 output
 //   KB (kb_relayout.hip) layout copies and transposes for the contraction's
 //                        gradients
+//   K3B (k3b_epilogue_grad.hip) backward of the epilogue: dL/dx, the gate
+//                        path's dL/dz and the epilogue's parameter gradients
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,12 +83,37 @@ struct RelayoutArgs {
   int64_t ld_q;           // >= round_up(rows, 64); columns rows .. round_up(rows, 64) get zeros
 };
 
+// K3B (k3b_epilogue_grad.hip): backward of the epilogue for a tile.
+struct K3BArgs {
+  const float *x;         // contraction result of the tile (x layout), as K3 reads it
+  int64_t ldx;
+  const void *z;          // [n][n][c_z] global
+  const uint8_t *mask;    // [n][n] global
+  int64_t n;
+  int64_t row_off, n_rows, col_off, n_cols;
+  const float *dout;      // [n_rows][n_cols][c_z] dL/dout
+  float *dx;              // dL/dx, x layout (may be x itself)
+  float *dz;              // [n_rows][n_cols][c_z] the gate path's share of dL/dz
+  const float *ln_out_w, *ln_out_b, *ln_in_w, *ln_in_b;
+  float eps;
+  const void *w_out_proj, *w_out_gate;
+  void *wt;               // workspace: W_out_proj^T, W_out_gate^T (element type)
+  float *part;            // workspace: kK3BMaxParts slots of kK3BSlotFloats
+  float *tot;             // workspace: one slot, the sums over all work-groups
+  int32_t n_parts;        // work-groups (set by the launcher)
+  float *g_w_out_proj, *g_w_out_gate, *g_ln_out_w, *g_ln_out_b, *g_ln_in_w, *g_ln_in_b;
+};
+// Slot of one work-group's partial sums: G [128][128], H [128][128], S [128], T [128].
+constexpr int kK3BSlotFloats = 2 * 128 * 128 + 2 * 128;
+constexpr int kK3BMaxParts = 256;
+
 // Each launcher checks the launch with hipGetLastError.  dtype is
 // TRIMUL_F32 or TRIMUL_BF16.
 hipError_t launch_k1(const K1Args &a, int dtype, hipStream_t s);
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s);
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s);
 hipError_t launch_relayout(const RelayoutArgs &a, bool from_x, int dtype, hipStream_t s);
+hipError_t launch_k3b(K3BArgs a, int dtype, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

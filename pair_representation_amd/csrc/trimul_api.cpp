@@ -501,6 +501,93 @@ trimul_status_t trimul_tile_backward(const trimul_weights_t *w, int64_t n_rows, 
   return ok();
 }
 
+namespace {
+
+struct EpilogueBackwardLayout {
+  size_t wt_off, tot_off, part_off, total;
+};
+
+EpilogueBackwardLayout epilogue_backward_layout(int32_t dtype) {
+  EpilogueBackwardLayout L;
+  const size_t slot = align256((size_t)trimul::kK3BSlotFloats * sizeof(float));
+  L.wt_off = 0;
+  L.tot_off = align256((size_t)2 * 128 * 128 * elt_bytes(dtype));
+  L.part_off = L.tot_off + slot;
+  L.total = L.part_off + (size_t)trimul::kK3BMaxParts * slot;
+  return L;
+}
+
+}  // namespace
+
+size_t trimul_epilogue_backward_workspace_bytes(const trimul_weights_t *w) {
+  if (check_weights(w) != TRIMUL_OK) return 0;
+  return epilogue_backward_layout(w->dtype).total;
+}
+
+trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, int64_t row_off, int64_t n_rows,
+                                         int64_t col_off, int64_t n_cols, const float *x_acc, const void *z,
+                                         const uint8_t *mask, const float *dout, float *dx, float *dz,
+                                         const trimul_epilogue_grads_t *grads, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (n < 1 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [1, %lld]", (long long)n, (long long)kMaxN);
+  if (row_off < 0 || n_rows < 1 || row_off + n_rows > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "row range [%lld, +%lld) outside [0, %lld)", (long long)row_off, (long long)n_rows, (long long)n);
+  if (col_off < 0 || n_cols < 1 || col_off + n_cols > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "col range [%lld, +%lld) outside [0, %lld)", (long long)col_off, (long long)n_cols, (long long)n);
+  if (!x_acc || !z || !mask || !dout || !dx || !dz)
+    return fail(TRIMUL_ERR_INVALID_ARG, "x_acc, z, mask, dout, dx and dz are required");
+  if (!aligned(x_acc, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16))
+    return fail(TRIMUL_ERR_ALIGNMENT, "x_acc, z, dout, dx and dz must be 16-byte aligned");
+  if (!grads) return fail(TRIMUL_ERR_INVALID_ARG, "grads is NULL");
+  float *const gp[] = {grads->w_out_proj, grads->w_out_gate, grads->ln_out_w, grads->ln_out_b, grads->ln_in_w, grads->ln_in_b};
+  const char *gn[] = {"w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b"};
+  for (int i = 0; i < 6; ++i) {
+    if (!gp[i]) return fail(TRIMUL_ERR_INVALID_ARG, "gradient %s is NULL", gn[i]);
+    if (!aligned(gp[i], 16)) return fail(TRIMUL_ERR_ALIGNMENT, "gradient %s is not 16-byte aligned", gn[i]);
+  }
+  const EpilogueBackwardLayout L = epilogue_backward_layout(w->dtype);
+  if (!workspace) return fail(TRIMUL_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  trimul::K3BArgs a{};
+  a.x = x_acc;
+  a.ldx = x_ld(n_cols);
+  a.z = z;
+  a.mask = mask;
+  a.n = n;
+  a.row_off = row_off;
+  a.n_rows = n_rows;
+  a.col_off = col_off;
+  a.n_cols = n_cols;
+  a.dout = dout;
+  a.dx = dx;
+  a.dz = dz;
+  a.ln_out_w = w->ln_out_w;
+  a.ln_out_b = w->ln_out_b;
+  a.ln_in_w = w->ln_in_w;
+  a.ln_in_b = w->ln_in_b;
+  a.eps = w->ln_eps;
+  a.w_out_proj = w->w_out_proj;
+  a.w_out_gate = w->w_out_gate;
+  a.wt = ws + L.wt_off;
+  a.tot = reinterpret_cast<float *>(ws + L.tot_off);
+  a.part = reinterpret_cast<float *>(ws + L.part_off);
+  a.g_w_out_proj = grads->w_out_proj;
+  a.g_w_out_gate = grads->w_out_gate;
+  a.g_ln_out_w = grads->ln_out_w;
+  a.g_ln_out_b = grads->ln_out_b;
+  a.g_ln_in_w = grads->ln_in_w;
+  a.g_ln_in_b = grads->ln_in_b;
+  const hipError_t e = trimul::launch_k3b(a, w->dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "epilogue backward kernel launch");
+  return ok();
+}
+
 const char *trimul_status_string(trimul_status_t s) {
   switch (s) {
     case TRIMUL_OK: return "ok";

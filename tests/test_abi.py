@@ -245,6 +245,57 @@ def test_backward_validation():
     assert str(need) in L.trimul_last_error().decode()
 
 
+def call_ebwd(w=None, n=100, row_off=10, n_rows=50, col_off=20, n_cols=40, x=FAKE, z=FAKE + 0x1000000,
+              mask=FAKE + 0x2000000, dout=FAKE + 0x3000000, dx=FAKE + 0x4000000, dz=FAKE + 0x5000000,
+              grads="ok", null_grad=None, misalign_grad=None, ws=FAKE + 0x8000000, ws_bytes=None):
+    L = pra.lib()
+    w = weights() if w is None else w
+    g = pra._EpilogueGrads(*[FAKE + 0x6000000 + 0x10000 * i for i in range(6)])
+    if null_grad:
+        setattr(g, null_grad, None)
+    if misalign_grad:
+        setattr(g, misalign_grad, FAKE + 0x6800000 + 4)
+    gp = ctypes.byref(g) if grads == "ok" else None
+    if ws_bytes is None:
+        ws_bytes = L.trimul_epilogue_backward_workspace_bytes(ctypes.byref(w))
+    return L.trimul_epilogue_backward(ctypes.byref(w), n, row_off, n_rows, col_off, n_cols, x, z, mask, dout, dx,
+                                      dz, gp, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("dtype,elt", [(pra.BF16, 2), (pra.F32, 4)])
+def test_epilogue_backward_workspace_closed_form(dtype, elt):
+    # transposed W_out_proj and W_out_gate, then one slot of sums plus 256
+    # per-work-group slots: G and H (128 x 128 fp32 each), S and T (128 each)
+    slot = round_up((2 * 128 * 128 + 2 * 128) * 4, 256)
+    want = round_up(2 * 128 * 128 * elt, 256) + slot + 256 * slot
+    assert pra.lib().trimul_epilogue_backward_workspace_bytes(ctypes.byref(weights(dtype))) == want
+    assert pra.lib().trimul_epilogue_backward_workspace_bytes(ctypes.byref(weights(dtype, c=64))) == 0
+
+
+def test_epilogue_backward_validation():
+    assert call_ebwd(w=weights(c_z=64)) == pra.ERR_UNSUPPORTED
+    assert call_ebwd(w=weights(null="w_out_gate")) == pra.ERR_INVALID_ARG
+    assert call_ebwd(n=0) == pra.ERR_INVALID_ARG
+    assert call_ebwd(n=70000) == pra.ERR_INVALID_ARG
+    assert call_ebwd(row_off=60) == pra.ERR_INVALID_ARG          # rows past n
+    assert call_ebwd(n_cols=0) == pra.ERR_INVALID_ARG
+    assert call_ebwd(col_off=-1) == pra.ERR_INVALID_ARG
+    for name in ("x", "z", "mask", "dout", "dx", "dz"):
+        assert call_ebwd(**{name: None}) == pra.ERR_INVALID_ARG, name
+    for name in ("x", "z", "dout", "dx", "dz"):
+        assert call_ebwd(**{name: FAKE + 0x9000000 + 8}) == pra.ERR_ALIGNMENT, name
+    assert call_ebwd(grads=None) == pra.ERR_INVALID_ARG
+    for name in ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b"):
+        assert call_ebwd(null_grad=name) == pra.ERR_INVALID_ARG, name
+        assert call_ebwd(misalign_grad=name) == pra.ERR_ALIGNMENT, name
+    assert call_ebwd(ws=None) == pra.ERR_INVALID_ARG
+    assert call_ebwd(ws=FAKE + 0x40) == pra.ERR_ALIGNMENT
+    L = pra.lib()
+    need = L.trimul_epilogue_backward_workspace_bytes(ctypes.byref(weights()))
+    assert call_ebwd(ws_bytes=need - 1) == pra.ERR_WORKSPACE_TOO_SMALL
+    assert str(need) in L.trimul_last_error().decode()
+
+
 def test_status_strings():
     L = pra.lib()
     for s in range(6):
