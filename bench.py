@@ -259,6 +259,101 @@ def cpu_baseline_backward(work, block_rows, block_k=128):
                       f"{n}x{n} grid ({t_full:.0f}s)"}
 
 
+def bench_epilogue_backward(work, args, dev):
+    """Backward of the epilogue (trimul_epilogue_backward) on the whole N x N
+    grid as one tile: x is the workload's real contraction result (K1 + K2 on
+    the seeded z, outgoing) and dout a seeded N(0,1) gradient; timed with HIP
+    events on the launch stream around the entry point (transpose of the two
+    matrices, the per-pair kernel, the two reduction kernels).  The rate counts
+    the N^2 pairs per call; the roofline is HBM: per pair the kernel reads x
+    (512 B), z (256 B bf16), the mask (1 B) and dout (512 B) and writes dx and
+    dz (512 B each), 2305 B, while its six 128 x 128 products (196608 flop per
+    pair) need a quarter of that time at the matrix-core peak."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    n = work.n
+    log(f"[bench] generating {work.name} (N={n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    kp = (n + 63) // 64 * 64
+    a_pl, b_pl = pra.tile_operands(w, pra.OUTGOING, z, mask, 0, n, 0, n, 0, n, kp)
+    x = pra.new_xacc(n, n, dev)
+    pra.tile(w, n, 0, n, 0, n, [(0, n, a_pl, b_pl)], pra.TILE_FIRST, x)
+    del a_pl, b_pl
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev).manual_seed(23456)
+    dout = torch.randn((n, n, C_Z), generator=g, device=dev)
+    dx = pra.new_xacc(n, n, dev)
+    dz = torch.empty((n, n, C_Z), dtype=torch.float32, device=dev)
+    grads = {k: torch.empty(shp, dtype=torch.float32, device=dev) for k, shp in pra.EPILOGUE_GRAD_SHAPES.items()}
+    ws = torch.empty(pra.epilogue_backward_workspace_bytes(w), dtype=torch.uint8, device=dev)
+
+    def call():
+        pra.epilogue_backward(w, n, 0, n, 0, n, x, z, mask, dout, dx, dz, grads, ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} epilogue-backward calls")
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        call()
+        e[1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    t = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e-3
+    per_pair = 512 + (256 if work.dtype == "bf16" else 512) + 1 + 512 + 512 + 512
+    nbytes = float(per_pair) * n * n
+    rec = {
+        "metric": "TriMul epilogue-backward pairs/s (dx, gate-path dz, parameter gradients) at N=3605, c=128 bf16 "
+                  "(1 GPU)",
+        "value": n * n / t, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": work.dtype, "data": "synthetic (x from the workload's own contraction; seeded N(0,1) dout)",
+        "config": {"workload": work.name, "n": n, "part": "epilogue backward, one tile"},
+        "roofline": {"bound": "hbm", "kernel": "trimul_epilogue_backward (whole call)",
+                     "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": nbytes / t / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_per_launch": f"{per_pair} B/pair * N^2 = {nbytes:.4e} B", "avg_launch_ms": t * 1e3},
+        "cpu_baseline": None,
+    }
+    del x, dout, dx, dz, ws, z, mask
+    torch.cuda.empty_cache()
+    if args.cpu_rows > 0:
+        rec["cpu_baseline"] = cpu_baseline_epilogue_backward(work, wts)
+    return rec
+
+
+def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
+    """oracle.finish_vjp (numpy float64 on the host cores) on ``blocks``
+    blocks of ``block`` seeded pairs, extrapolated to the N^2 pairs."""
+    import numpy as np
+
+    import oracle
+
+    r = np.random.default_rng(6)
+    wref = {k: v.double().cpu().numpy() for k, v in wts.items()}
+    t_sum = 0.0
+    for _ in range(blocks):
+        x = r.standard_normal((block, C))
+        zz = r.standard_normal((block, C_Z))
+        m = (r.random(block) < 0.9).astype(np.uint8)
+        d = r.standard_normal((block, C_Z))
+        t0 = time.perf_counter()
+        oracle.finish_vjp(x, zz, m, wref, d)
+        t_sum += time.perf_counter() - t0
+    rate = block * blocks / t_sum
+    n = work.n
+    return {"value": rate, "unit": "pairs/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"oracle.finish_vjp on {blocks} blocks of {block} seeded pairs ({t_sum:.2f}s); the "
+                      f"{n}x{n} grid would take {n * n / rate:.0f}s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,9 +361,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "backward"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "backward", "epilogue-backward"],
                     help="copy: run a plain device copy of known size (HBM counter calibration); "
-                         "backward: the contraction step's gradients (trimul_tile_backward)")
+                         "backward: the contraction step's gradients (trimul_tile_backward); "
+                         "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -295,6 +391,9 @@ def main():
     work = wl.WORKLOADS[args.workload]
     if args.mode == "backward":
         print(json.dumps(bench_backward(work, args, dev)), flush=True)
+        return
+    if args.mode == "epilogue-backward":
+        print(json.dumps(bench_epilogue_backward(work, args, dev)), flush=True)
         return
     if work.tile:
         print(json.dumps(bench_tile(work, args, dev)), flush=True)

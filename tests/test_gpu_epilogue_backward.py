@@ -3,10 +3,16 @@ the oracle's gradients (oracle.finish_vjp), through the C ABI.
 
 The inputs are exact in the storage dtype (z and the two matrices bf16 in bf16
 mode) and the oracle gets those exact values.  Every product on the matrix
-cores keeps fp32-level accuracy (bf16 mode: each non-weight operand split into
-two bf16 terms, the lo*lo term dropped, relative error below about 2^-16 per
-product), accumulation is fp32, so the bar is 1e-4 of the rms of each
-gradient in both modes (fp32 mode is well inside it).
+cores keeps fp32-level accuracy: in bf16 mode each non-weight operand is split
+into hi = bf16(v) and lo = bf16(v - hi) (representation error <= 2^-18 |v|)
+and the lo*lo term is dropped, so one product is off by at most about
+3 * 2^-18 = 1.1e-5 of its size; accumulation is fp32.  Bars, as
+max |diff| / rms(ref):
+  dx, dz (each entry a short sum of such products)         1e-4
+  parameter gradients                                      3e-4
+the latter because a gradient summed over few pairs is close to a rank-1
+outer product, whose largest entries are 10-25 times its rms, and each entry
+carries the per-product relative error.  fp32 mode is well inside both.
 
 x_acc is filled with NaN outside the tile's pairs: the padding of the
 accumulator layout must never reach a gradient.
@@ -24,7 +30,8 @@ from tests.gpu_util import rel_err
 pytestmark = pytest.mark.gpu
 
 C = 128
-TOL = 1e-4
+TOL = {"x": 1e-4, "z": 1e-4}
+TOL_PARAM = 3e-4
 NAMES = ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b")
 
 
@@ -80,7 +87,7 @@ def run_case(dev, dtype, n, row_off, n_rows, col_off, n_cols, seed, in_place=Fal
     keep = mt != 0
     assert np.all(got["x"][~keep] == 0) and np.all(got["z"][~keep] == 0)
     for k, v in errs.items():
-        assert v <= TOL, (k, v)
+        assert v <= TOL.get(k, TOL_PARAM), (k, v)
     return got
 
 
@@ -146,7 +153,7 @@ def test_epilogue_backward_full_size_sparse_dout(dev):
     errs = {k: rel_err(got[k], ref[k]) for k in ref}
     print("  errors: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
-        assert v <= TOL, (k, v)
+        assert v <= TOL.get(k, TOL_PARAM), (k, v)
     # pairs with dout = 0 get exactly zero gradients
     I0 = torch.as_tensor(r.integers(0, n, 400), device=dev)
     J0 = torch.as_tensor(r.integers(0, n, 400), device=dev)
