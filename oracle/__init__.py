@@ -22,7 +22,8 @@ Modules
 -------
 trimul_ref   vectorised float64 definition, Q-mode (bf16 contraction operands),
              blockwise and sampled evaluation, tile partial sums, and the
-             gradients of the contraction step and of the epilogue.
+             gradients of the projections, the contraction step, the
+             epilogue and the whole layer.
 bruteforce   per-element scalar loops of the same definition, for tiny inputs.
 
 Parity status: every function here is pinned by the CPU tests in
@@ -42,9 +43,11 @@ from .trimul_ref import (  # noqa: F401
     finish_vjp,
     layer_norm,
     project,
+    project_vjp,
     sigmoid,
     tile_partial,
     trimul,
     trimul_blockwise,
+    trimul_vjp,
     trimul_sampled,
 )

@@ -251,6 +251,79 @@ def trimul(z, mask, w, direction, quant=False, eps=LN_EPS, return_x=False):
     return (out, x) if return_x else out
 
 
+def project_vjp(z, mask, w, da, db, eps=LN_EPS):
+    """Gradients of L = sum(da * a) + sum(db * b) with (a, b) = project(z,
+    mask, w) (exact, no rounding): the backward of the gated a/b projections.
+    Returns a dict with keys z (the projections' share of dL/dz), w_a_proj,
+    w_a_gate, w_b_proj, w_b_gate, ln_in_w, ln_in_b (the projections' share).
+    float64, the forward's steps backwards, per side s in (a, b):
+
+        zh = LN(z) = zhh*g_i + b_i,  u = W_sp zh,  v = W_sg zh,
+        g = sigmoid(v),  s = m * g * u
+        du = m*g*ds,  dv = m*u*ds * g*(1 - g)
+        dW_sp = sum du (x) zh,  dW_sg = sum dv (x) zh
+        dzh = sum over sides of (W_sp^T du + W_sg^T dv)
+        dg_i = sum dzh*zhh,  db_i = sum dzh,  dz = LN backward of dzh*g_i
+    (sums over all pairs).  Page 1 (section "Pra quem e") expects the layer to
+    be trained through custom autograd functions; this is the projections'
+    part.
+    """
+    z = _f64(z)
+    m = (_f64(mask) != 0).astype(np.float64)[..., None]
+    zhh, rz = _ln_parts(z, eps)
+    zh = zhh * _f64(w["ln_in_w"]) + _f64(w["ln_in_b"])
+    cz = zh.shape[-1]
+    zh2 = zh.reshape(-1, cz)
+    out = {}
+    dzh = np.zeros_like(zh)
+    for side, ds in (("a", _f64(da)), ("b", _f64(db))):
+        wp, wg = _f64(w[f"w_{side}_proj"]), _f64(w[f"w_{side}_gate"])
+        u = _lin(zh, wp)
+        g = sigmoid(_lin(zh, wg))
+        du = m * g * ds
+        dv = m * u * ds * g * (1.0 - g)
+        c = u.shape[-1]
+        out[f"w_{side}_proj"] = du.reshape(-1, c).T @ zh2
+        out[f"w_{side}_gate"] = dv.reshape(-1, c).T @ zh2
+        dzh = dzh + du @ wp + dv @ wg
+    out["z"] = _ln_vjp(dzh * _f64(w["ln_in_w"]), zhh, rz)
+    out["ln_in_w"] = (dzh * zhh).reshape(-1, cz).sum(axis=0)
+    out["ln_in_b"] = dzh.reshape(-1, cz).sum(axis=0)
+    return out
+
+
+def trimul_vjp(z, mask, w, direction, dout, eps=LN_EPS):
+    """Gradients of L = sum(dout * trimul(z, mask, w, direction)) (exact) with
+    respect to z and every parameter (keys z and WEIGHT_KEYS): the whole
+    layer's backward, composed of the three steps' gradients in reverse order
+    -- finish_vjp (epilogue), contract_rows_vjp (the k-contraction; incoming
+    contracts the transposed operands) and project_vjp (projections) -- with
+    dL/dz and the input LayerNorm's parameters summed over the gate path and
+    the projections.  Page 1 (section "Pra quem e") expects the layer to be
+    trained through custom autograd functions; this is its full gradient.
+    """
+    a, b = project(z, mask, w, False, eps)
+    x = contract(a, b, direction)
+    ge = finish_vjp(x, z, mask, w, dout, eps)
+    if direction == "outgoing":
+        da, db = contract_rows_vjp(a, b, ge["x"])
+    elif direction == "incoming":
+        dat, dbt = contract_rows_vjp(np.swapaxes(a, 0, 1), np.swapaxes(b, 0, 1), ge["x"])
+        da, db = np.swapaxes(dat, 0, 1), np.swapaxes(dbt, 0, 1)
+    else:
+        raise ValueError(f"unknown direction {direction!r}")
+    gp = project_vjp(z, mask, w, da, db, eps)
+    return {
+        "z": ge["z"] + gp["z"],
+        "ln_in_w": ge["ln_in_w"] + gp["ln_in_w"],
+        "ln_in_b": ge["ln_in_b"] + gp["ln_in_b"],
+        "w_a_proj": gp["w_a_proj"], "w_a_gate": gp["w_a_gate"],
+        "w_b_proj": gp["w_b_proj"], "w_b_gate": gp["w_b_gate"],
+        "w_out_gate": ge["w_out_gate"], "ln_out_w": ge["ln_out_w"], "ln_out_b": ge["ln_out_b"],
+        "w_out_proj": ge["w_out_proj"],
+    }
+
+
 # ---------------------------------------------------------------------------
 # Evaluation on parts of the grid.  Every output pair (i, j) needs only the
 # operand rows i and j (outgoing) or the operand columns i and j (incoming),

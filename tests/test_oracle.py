@@ -512,3 +512,108 @@ def test_finish_vjp_special_cases():
     want = (0.5 * m[:, None] * dout).T @ n
     assert np.max(np.abs(g2["w_out_proj"] - want)) < 1e-12
     assert np.max(np.abs(g2["z"])) == 0
+
+
+def _proj_case(seed, p=6, c=5, cz=7, keep=0.7):
+    r = np.random.default_rng(seed)
+    w = {"ln_in_w": 1 + 0.3 * r.standard_normal(cz), "ln_in_b": 0.2 * r.standard_normal(cz)}
+    for k in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate"):
+        w[k] = r.standard_normal((c, cz)) / np.sqrt(cz)
+    z = r.standard_normal((p, cz)) * 1.5 + 0.3
+    m = (r.random(p) < keep).astype(np.uint8)
+    m[0] = 1
+    da = r.standard_normal((p, c))
+    db = r.standard_normal((p, c))
+    return z, m, w, da, db
+
+
+def test_project_vjp_finite_differences():
+    z, m, w, da, db = _proj_case(31)
+    g = oracle.project_vjp(z, m, w, da, db)
+
+    def L(z_, w_):
+        a, b = oracle.project(z_, m, w_)
+        return float(np.sum(da * a) + np.sum(db * b))
+
+    r = np.random.default_rng(32)
+    h = 1e-5
+    v = r.standard_normal(z.shape)
+    fd = (L(z + h * v, w) - L(z - h * v, w)) / (2 * h)
+    assert abs(fd - float(np.sum(g["z"] * v))) < 1e-7 * (1 + abs(fd))
+    for key in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate", "ln_in_w", "ln_in_b"):
+        v = r.standard_normal(np.shape(w[key]))
+        wp = dict(w); wp[key] = w[key] + h * v
+        wm = dict(w); wm[key] = w[key] - h * v
+        fd = (L(z, wp) - L(z, wm)) / (2 * h)
+        assert abs(fd - float(np.sum(g[key] * v))) < 1e-7 * (1 + abs(fd)), key
+
+
+def test_project_vjp_special_cases():
+    z, m, w, da, db = _proj_case(33)
+    g = oracle.project_vjp(z, m, w, da, db)
+    # the input LayerNorm removes a common shift: each pair's dz sums to 0
+    assert np.max(np.abs(g["z"].sum(axis=-1))) < 1e-12
+    # every pair masked: a = b = 0 identically, so is every gradient
+    g0 = oracle.project_vjp(z, np.zeros_like(m), w, da, db)
+    assert all(np.max(np.abs(v)) == 0 for v in g0.values())
+    # db = 0: nothing flows through the b side
+    gb = oracle.project_vjp(z, m, w, da, np.zeros_like(db))
+    assert np.max(np.abs(gb["w_b_proj"])) == 0 and np.max(np.abs(gb["w_b_gate"])) == 0
+    # gates at zero: sigmoid = 1/2 and its slope 1/4, so with zh = LN(z)
+    #   dW_ap = sum (m/2) da (x) zh,  dW_ag = sum (m/4) (W_ap zh) da (x) zh
+    w0 = dict(w); w0["w_a_gate"] = np.zeros_like(w["w_a_gate"]); w0["w_b_gate"] = np.zeros_like(w["w_b_gate"])
+    g0 = oracle.project_vjp(z, m, w0, da, db)
+    zh = oracle.layer_norm(z, w["ln_in_w"], w["ln_in_b"])
+    mm = m[:, None].astype(np.float64)
+    assert np.max(np.abs(g0["w_a_proj"] - (0.5 * mm * da).T @ zh)) < 1e-12
+    assert np.max(np.abs(g0["w_a_gate"] - (0.25 * mm * (zh @ w["w_a_proj"].T) * da).T @ zh)) < 1e-12
+
+
+def _layer_case(seed, n=4, c=5, cz=6, keep=0.8):
+    r = np.random.default_rng(seed)
+    w = {"ln_in_w": 1 + 0.3 * r.standard_normal(cz), "ln_in_b": 0.2 * r.standard_normal(cz),
+         "ln_out_w": 1 + 0.3 * r.standard_normal(c), "ln_out_b": 0.2 * r.standard_normal(c),
+         "w_out_proj": r.standard_normal((cz, c)) / np.sqrt(c), "w_out_gate": r.standard_normal((cz, cz)) / np.sqrt(cz)}
+    for k in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate"):
+        w[k] = r.standard_normal((c, cz)) / np.sqrt(cz)
+    z = r.standard_normal((n, n, cz)) + 0.2
+    m = (r.random((n, n)) < keep).astype(np.uint8)
+    m[0, 0] = 1
+    dout = r.standard_normal((n, n, cz))
+    return z, m, w, dout
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_trimul_vjp_finite_differences(direction):
+    """The whole layer's gradient against central differences of the
+    forward definition, for z and every parameter."""
+    z, m, w, dout = _layer_case(41)
+    g = oracle.trimul_vjp(z, m, w, direction, dout)
+    L = lambda z_, w_: float(np.sum(dout * oracle.trimul(z_, m, w_, direction)))
+    r = np.random.default_rng(42)
+    h = 1e-5
+    v = r.standard_normal(z.shape)
+    fd = (L(z + h * v, w) - L(z - h * v, w)) / (2 * h)
+    assert abs(fd - float(np.sum(g["z"] * v))) < 1e-6 * (1 + abs(fd))
+    for key in oracle.WEIGHT_KEYS:
+        v = r.standard_normal(np.shape(w[key]))
+        wp = dict(w); wp[key] = w[key] + h * v
+        wm = dict(w); wm[key] = w[key] - h * v
+        fd = (L(z, wp) - L(z, wm)) / (2 * h)
+        assert abs(fd - float(np.sum(g[key] * v))) < 1e-6 * (1 + abs(fd)), key
+
+
+def test_trimul_vjp_transpose_relation():
+    """incoming(z, m; W) = outgoing(z^T, m^T; W with a <-> b swapped)^T, so the
+    incoming gradients are the outgoing ones of that problem: dz transposed,
+    the a and b weights' gradients swapped, the rest equal."""
+    z, m, w, dout = _layer_case(43)
+    ws = dict(w)
+    ws["w_a_proj"], ws["w_b_proj"] = w["w_b_proj"], w["w_a_proj"]
+    ws["w_a_gate"], ws["w_b_gate"] = w["w_b_gate"], w["w_a_gate"]
+    gi = oracle.trimul_vjp(z, m, w, "incoming", dout)
+    go = oracle.trimul_vjp(np.swapaxes(z, 0, 1), m.T, ws, "outgoing", np.swapaxes(dout, 0, 1))
+    assert np.max(np.abs(gi["z"] - np.swapaxes(go["z"], 0, 1))) < 1e-12
+    swap = {"w_a_proj": "w_b_proj", "w_b_proj": "w_a_proj", "w_a_gate": "w_b_gate", "w_b_gate": "w_a_gate"}
+    for key in oracle.WEIGHT_KEYS:
+        assert np.max(np.abs(gi[key] - go[swap.get(key, key)])) < 1e-10, key
