@@ -46,7 +46,8 @@
  * normalised input and the a/b operands are rounded to bf16 (nearest-even)
  * for the bf16 matrix-core projection and contraction; the output LayerNorm
  * result and the normalised input feeding the output gate are split into two
- * bf16 terms (hi + lo) so the epilogue products keep fp32-level accuracy.  The
+ * bf16 terms (hi + lo, together within 2^-16 of the value) so the epilogue
+ * products keep about 16 significant bits instead of bf16's 8.  The
  * output is fp32 in both modes.
  */
 #ifndef TRIMUL_H
@@ -73,6 +74,9 @@ typedef enum { TRIMUL_OUTGOING = 0, TRIMUL_INCOMING = 1 } trimul_dir_t;
 
 /* Flags of trimul_tile. */
 enum { TRIMUL_TILE_FIRST = 1u, TRIMUL_TILE_LAST = 2u };
+/* Flag of trimul_tile_operands_backward: add the parameter gradients to the
+ * grads buffers instead of overwriting them. */
+enum { TRIMUL_GRAD_ACCUMULATE = 1u };
 
 /* Largest number of k-chunks one trimul_tile call accepts. */
 #define TRIMUL_MAX_CHUNKS 32
@@ -269,6 +273,52 @@ trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, i
                                          const float *dout, float *dx, float *dz,
                                          const trimul_epilogue_grads_t *grads /* (host) */,
                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Parameter gradients of the a/b projections, fp32. */
+typedef struct {
+  float *w_a_proj;             /* [c][c_z] dL/dW_a_proj (used when da != NULL)  */
+  float *w_a_gate;             /* [c][c_z] dL/dW_a_gate (used when da != NULL)  */
+  float *w_b_proj;             /* [c][c_z] dL/dW_b_proj (used when db != NULL)  */
+  float *w_b_gate;             /* [c][c_z] dL/dW_b_gate (used when db != NULL)  */
+  float *ln_in_w;              /* [c_z] the projections' share of
+                                        dL/d(input LayerNorm gamma)             */
+  float *ln_in_b;              /* [c_z] the same for beta                       */
+} trimul_projection_grads_t;
+
+/* Backward of trimul_tile_operands: the step that turns the gradients of one
+ * operand chunk into gradients of z and of the projection parameters (page 1,
+ * section "Pra quem e": the layer is trained through custom autograd
+ * functions).  With zh = LN(z; ln_in) and, per side s in {a, b},
+ *   s = m * sigmoid(W_s_gate zh) * (W_s_proj zh)
+ * at the source pair of each operand entry (layout of trimul_tile_operands:
+ * a row r <-> residue row_off + r, b row s <-> col_off + s, column t <->
+ * residue k_off + t; outgoing pairs (row, k), incoming (k, row)), given
+ *   da = dL/da_chunk, fp32 in the x_acc layout with rows n_rows, columns
+ *        k_len (trimul_tile_xacc_bytes(w, n_rows, k_len); as
+ *        trimul_tile_backward writes it), or NULL (side a skipped)
+ *   db = dL/db_chunk likewise with rows n_cols, or NULL (not both NULL)
+ * it ADDS to dz ([n][n][c_z] fp32, the global pair tensor's gradient; the
+ * caller zeroes it or passes the epilogue's share) the projections' share of
+ * dL/dz at every source pair, and writes the parameter gradients (sums over
+ * the chunk's entries; masked entries contribute nothing), or adds them with
+ * TRIMUL_GRAD_ACCUMULATE.  grads->w_a_* are used only with da, w_b_* only with
+ * db; ln_in_* receive both sides' shares.  Everything is linear in (da, db),
+ * so several chunks, tiles or sides may be fed by separate calls.  The
+ * parameter gradients use the same G/S construction as
+ * trimul_epilogue_backward (both projections of a side share the one input
+ * LayerNorm); precision as there (fixed summation order).  Calls on one
+ * stream run in order; the same dz must not be updated by concurrent calls.
+ * workspace >= trimul_tile_operands_backward_workspace_bytes(w) bytes,
+ * 256-byte aligned; contents on entry are ignored. */
+size_t trimul_tile_operands_backward_workspace_bytes(const trimul_weights_t *w);
+
+trimul_status_t trimul_tile_operands_backward(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                              const uint8_t *mask, int64_t n, int64_t row_off,
+                                              int64_t n_rows, int64_t col_off, int64_t n_cols,
+                                              int64_t k_off, int64_t k_len, const float *da,
+                                              const float *db, float *dz, uint32_t flags,
+                                              const trimul_projection_grads_t *grads /* (host) */,
+                                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *trimul_status_string(trimul_status_t s);

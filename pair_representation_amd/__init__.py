@@ -16,6 +16,8 @@ Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     tile_backward(w, n_rows, n_cols, chunks, dx, ...)
     epilogue_backward_workspace_bytes(w)
     epilogue_backward(w, n, row_off, n_rows, col_off, n_cols, x_acc, z, mask, dout, ...)
+    tile_operands_backward_workspace_bytes(w)
+    tile_operands_backward(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, da, db, dz, ...)
 """
 
 from __future__ import annotations
@@ -67,6 +69,15 @@ class _EpilogueGrads(ctypes.Structure):
                 ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b")]
 
 
+class _ProjectionGrads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate", "ln_in_w", "ln_in_b")]
+
+
+PROJECTION_GRAD_SHAPES = {"w_a_proj": (C, C_Z), "w_a_gate": (C, C_Z), "w_b_proj": (C, C_Z), "w_b_gate": (C, C_Z),
+                          "ln_in_w": (C_Z,), "ln_in_b": (C_Z,)}
+GRAD_ACCUMULATE = 1
+
 EPILOGUE_GRAD_SHAPES = {"w_out_proj": (C_Z, C), "w_out_gate": (C_Z, C_Z), "ln_out_w": (C,), "ln_out_b": (C,),
                         "ln_in_w": (C_Z,), "ln_in_b": (C_Z,)}
 
@@ -109,6 +120,11 @@ def lib():
         L.trimul_epilogue_backward.argtypes = [W, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                                ctypes.POINTER(_EpilogueGrads), vp, sz, vp]
         L.trimul_epilogue_backward.restype = ctypes.c_int
+        L.trimul_tile_operands_backward_workspace_bytes.argtypes = [W]
+        L.trimul_tile_operands_backward_workspace_bytes.restype = sz
+        L.trimul_tile_operands_backward.argtypes = [W, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                                    vp, vp, vp, u32, ctypes.POINTER(_ProjectionGrads), vp, sz, vp]
+        L.trimul_tile_operands_backward.restype = ctypes.c_int
         L.trimul_status_string.argtypes = [ctypes.c_int]
         L.trimul_status_string.restype = ctypes.c_char_p
         L.trimul_last_error.argtypes = []
@@ -398,3 +414,52 @@ def epilogue_backward(w: Weights, n, row_off, n_rows, col_off, n_cols, x_acc, z,
                                           _ptr(mask), _ptr(dout), _ptr(dx), _ptr(dz), ctypes.byref(g),
                                           _ptr(workspace), workspace.numel(), _stream()))
     return dx, dz, grads
+
+
+def tile_operands_backward_workspace_bytes(w: Weights) -> int:
+    return int(lib().trimul_tile_operands_backward_workspace_bytes(w.ref))
+
+
+def tile_operands_backward(w: Weights, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len,
+                           da=None, db=None, dz=None, grads=None, accumulate=False, workspace=None):
+    """Backward of tile_operands: adds the projections' share of dL/dz to
+    ``dz`` ([n, n, 128] fp32, zeros allocated if None) and writes (or with
+    ``accumulate`` adds) the projection parameters' gradients into ``grads``
+    (dict keyed as PROJECTION_GRAD_SHAPES; allocated if None).  ``da`` / ``db``
+    are the gradients of the chunk's operands in the accumulator layout
+    (xacc_shape(n_rows, k_len) / xacc_shape(n_cols, k_len)), as tile_backward
+    returns them; either may be None.  Returns (dz, grads)."""
+    n = z.shape[0]
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    if da is None and db is None:
+        raise ValueError("da and db are both None")
+    if da is not None:
+        _need(da, "da", torch.float32, xacc_shape(n_rows, k_len))
+    if db is not None:
+        _need(db, "db", torch.float32, xacc_shape(n_cols, k_len))
+    dev = z.device
+    if dz is None:
+        dz = torch.zeros((n, n, C_Z), dtype=torch.float32, device=dev)
+    _need(dz, "dz", torch.float32, (n, n, C_Z))
+    if grads is None:
+        grads = {k: torch.empty(shp, dtype=torch.float32, device=dev) for k, shp in PROJECTION_GRAD_SHAPES.items()}
+    ptrs = []
+    for k, shp in PROJECTION_GRAD_SHAPES.items():
+        used = (k.startswith("w_a") and da is not None) or (k.startswith("w_b") and db is not None) \
+            or k.startswith("ln_in")
+        if used:
+            _need(grads[k], f"grads[{k!r}]", torch.float32, shp)
+            ptrs.append(grads[k].data_ptr())
+        else:
+            ptrs.append(grads[k].data_ptr() if grads.get(k) is not None else None)
+    g = _ProjectionGrads(*ptrs)
+    need = tile_operands_backward_workspace_bytes(w)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib().trimul_tile_operands_backward(w.ref, direction, _ptr(z), _ptr(mask), n, row_off, n_rows, col_off,
+                                               n_cols, k_off, k_len, _ptr(da), _ptr(db), _ptr(dz),
+                                               GRAD_ACCUMULATE if accumulate else 0, ctypes.byref(g),
+                                               _ptr(workspace), workspace.numel(), _stream()))
+    return dz, grads

@@ -32,7 +32,8 @@
 // matrix-core operands (bf16 mode: hi + lo bf16 terms, as in K3), and x^, z^,
 // dy, dt as fp32 [channel][pair] planes, the operands of the G and H products
 // (contraction over pairs; split into hi + lo bf16 terms when read in bf16
-// mode, three products per step, so that G and H keep fp32-level accuracy).
+// mode, three products per step: hi = bf16(v), lo = bf16(v - hi) represent
+// v to within 2^-16 |v|, and the dropped lo*lo term is as small).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -225,7 +226,7 @@ __device__ __forceinline__ float2 merge8(const float2 (&pg)[kGroups], float eps)
   return make_float2(mean, rsqrt_f32((m2 + kPer * dev) * (1.0f / kC) + eps));
 }
 
-template <typename T>
+template <typename T, bool kProj>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k3b_epilogue_grad(K3BArgs p) {
   constexpr int E = sizeof(T);
   constexpr bool kWeightsInRegs = (E == 2);
@@ -252,14 +253,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int hl = lane >> 5;           // accumulator half: rows +4 of each group of 8
 
   for (int i = tid; i < kC; i += kThreads) {
-    ln[0][i] = p.ln_out_w[i];
-    ln[1][i] = p.ln_out_b[i];
-    ln[2][i] = p.ln_in_w[i];
-    ln[3][i] = p.ln_in_b[i];
+    ln[0][i] = p.ln_x_w[i];
+    ln[1][i] = p.ln_x_b[i];
+    ln[2][i] = p.ln_z_w[i];
+    ln[3][i] = p.ln_z_b[i];
   }
 
-  const T *const Wo = static_cast<const T *>(p.w_out_proj);
-  const T *const Wg = static_cast<const T *>(p.w_out_gate);
+  const T *const Wo = static_cast<const T *>(p.w_y);
+  const T *const Wg = static_cast<const T *>(p.w_t);
   const T *const WoT = static_cast<const T *>(p.wt);
   const T *const WgT = WoT + kC * kC;
   // A-operand fragment at k step ks of rows 32w .. +31 of a row-major 128 x 128
@@ -282,9 +283,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const unsigned char *zbytes = static_cast<const unsigned char *>(p.z);
 
   // ---- per-item loads, prefetched one item ahead ---------------------------
-  // Pairs outside the tile read a valid stand-in pair and are treated as
-  // masked; their x (padding of the x layout, unspecified) never reaches a
-  // sum.
+  // Positions outside the grid read a valid stand-in pair and are treated as
+  // masked; their x and dout (padding of the x layout, unspecified) never
+  // reach a sum.  Projection mode takes x from z (loaded once).
   float xv[kPer];
   ZRow<T> zr;
   f32x4 dv[4];
@@ -297,20 +298,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     ps.s0 += kCols;
     if (ps.s0 >= p.n_cols) { ps.s0 = 0; ++ps.blk; }
   };
+  // global pair index of grid position (r, c)
+  auto pair_of = [&](int64_t r, int64_t c) -> int64_t {
+    return p.transposed ? (p.col_off + c) * p.n + p.row_off + r : (p.row_off + r) * p.n + p.col_off + c;
+  };
   auto load_item = [&](const Pos &ps) {
-    const float *xp = p.x + x_offset(ps.blk * 4, ps.s0, c0, p.ldx) + q;
+    if constexpr (!kProj) {
+      const float *xp = p.x + x_offset(ps.blk * 4, ps.s0, c0, p.ldx) + q;
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) xv[c] = xp[c * 64];
+      for (int c = 0; c < kPer; ++c) xv[c] = xp[c * 64];
+    }
     const int64_t r = ps.blk * 4 + (q & 3), col = ps.s0 + (q >> 2);
     valid = r < p.n_rows && col < p.n_cols;
     const int64_t rr = r < p.n_rows ? r : p.n_rows - 1;
     const int64_t cc = col < p.n_cols ? col : p.n_cols - 1;
-    const int64_t g = (p.row_off + rr) * p.n + p.col_off + cc;
+    const int64_t g = pair_of(rr, cc);
     zr.load(zbytes + (g * kCz + c0) * E);
     mbyte = p.mask[g];
-    const float *dp = p.dout + (rr * p.n_cols + cc) * kCz + o0 + 4 * hl;
+    if constexpr (kProj) {
+      // the x layout: channel o of position (r, c) at x_offset(r, c, o) (the
+      // item's block exists in the buffer, padding included)
+      const float *dp = p.dout + x_offset(ps.blk * 4, ps.s0, o0, p.ldx) + q;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) dv[g4] = *reinterpret_cast<const f32x4 *>(dp + 8 * g4);
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv[g4][i] = dp[acc_row(4 * g4 + i, lane) * 64];
+    } else {
+      const float *dp = p.dout + (rr * p.n_cols + cc) * kCz + o0 + 4 * hl;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) dv[g4] = *reinterpret_cast<const f32x4 *>(dp + 8 * g4);
+    }
   };
 
   f32x16 G[4], H[4];
@@ -349,6 +366,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // ---- row layout: moments of x and z over this thread's 16 channels ----
     float zf[kPer];
     zr.to_f32(zf);
+    if constexpr (kProj) {
+#pragma unroll
+      for (int c = 0; c < kPer; ++c) xv[c] = zf[c];
+    }
     {
       const float2 mx = moments16(xv), mz = moments16(zf);
       part_f[grp][q] = make_float4(mx.x, mx.y, mz.x, mz.y);
@@ -517,22 +538,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const float mg = t.x * (1.0f / kC), mgx = t.y * (1.0f / kC);
       const float mh = t.z * (1.0f / kC), mhz = t.w * (1.0f / kC);
       const int64_t r = blk * 4 + (q & 3), col = s0 + (q >> 2);
-      float *const dzrow = p.dz + (r * p.n_cols + col) * kCz + o0 + 4 * hl;
-      float *const dxp = p.dx + x_offset(blk * 4, s0, o0, p.ldx) + q;
+      if constexpr (kProj) {
+        // one LayerNorm (x = z): dz = r (g + h - mean(g + h) - z^ mean((g + h) z^)),
+        // added to the pair's row of the global dz
+        float *const dzrow = p.dz + pair_of(r, col) * kCz + o0 + 4 * hl;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 vz;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 vz = *reinterpret_cast<const f32x4 *>(dzrow + 8 * g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g4 + i;
-          const int k = o0 + acc_row(e, lane);
-          // masked pairs: every term is zero (dn = dzh = 0, x^ = z^ = 0)
-          const float dxv = rx * (dy_pl[pl(k, q)] - mg - xh_pl[pl(k, q)] * mgx);
-          const float dzv = rz * (dt_pl[pl(k, q)] - mh - zh_pl[pl(k, q)] * mhz);
-          dxp[acc_row(e, lane) * 64] = keep ? dxv : 0.f;
-          vz[i] = keep ? dzv : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int k = o0 + acc_row(4 * g4 + i, lane);
+            const float v = rz * (dy_pl[pl(k, q)] + dt_pl[pl(k, q)] - (mg + mh) - zh_pl[pl(k, q)] * (mgx + mhz));
+            vz[i] += keep ? v : 0.f;
+          }
+          *reinterpret_cast<f32x4 *>(dzrow + 8 * g4) = vz;
         }
-        *reinterpret_cast<f32x4 *>(dzrow + 8 * g4) = vz;
+      } else {
+        float *const dzrow = p.dz + (r * p.n_cols + col) * kCz + o0 + 4 * hl;
+        float *const dxp = p.dx + x_offset(blk * 4, s0, o0, p.ldx) + q;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 vz;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g4 + i;
+            const int k = o0 + acc_row(e, lane);
+            // masked pairs: every term is zero (dn = dzh = 0, x^ = z^ = 0)
+            const float dxv = rx * (dy_pl[pl(k, q)] - mg - xh_pl[pl(k, q)] * mgx);
+            const float dzv = rz * (dt_pl[pl(k, q)] - mh - zh_pl[pl(k, q)] * mhz);
+            dxp[acc_row(e, lane) * 64] = keep ? dxv : 0.f;
+            vz[i] = keep ? dzv : 0.f;
+          }
+          *reinterpret_cast<f32x4 *>(dzrow + 8 * g4) = vz;
+        }
       }
     }
   }
@@ -555,10 +593,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-// W^T of the two epilogue matrices into the workspace (element type kept).
+// W^T of the two matrices into the workspace (element type kept).
 template <typename T>
-__global__ __launch_bounds__(256) void k3b_transpose(const T *wo, const T *wg, T *wt) {
-  const T *src = blockIdx.x == 0 ? wo : wg;
+__global__ __launch_bounds__(256) void k3b_transpose(const T *wy, const T *wt_, T *wt) {
+  const T *src = blockIdx.x == 0 ? wy : wt_;
   T *dst = wt + blockIdx.x * kC * kC;
   for (int i = threadIdx.x; i < kC * kC; i += 256) {
     const int o = i / kC, k = i % kC;
@@ -566,7 +604,8 @@ __global__ __launch_bounds__(256) void k3b_transpose(const T *wo, const T *wg, T
   }
 }
 
-// Sum of the slots (fixed order) and the weight-matrix gradients.
+// Sum of the slots (fixed order) and the weight-matrix gradients
+//   dW_y = G diag(g_x) + S b_x^T,  dW_t = H diag(g_z) + T b_z^T.
 // Work-group (m, o): row o of G (m = 0) or H (m = 1); thread k: column k.
 __global__ __launch_bounds__(kC) void k3b_reduce(K3BArgs p) {
   const int m = blockIdx.x / kC, o = blockIdx.x % kC, k = threadIdx.x;
@@ -578,14 +617,17 @@ __global__ __launch_bounds__(kC) void k3b_reduce(K3BArgs p) {
   }
   p.tot[m * kC * kC + o * kC + k] = acc;
   if (k == 0) p.tot[2 * kC * kC + m * kC + o] = sv;
-  const float *gam = m == 0 ? p.ln_out_w : p.ln_in_w;
-  const float *bet = m == 0 ? p.ln_out_b : p.ln_in_b;
-  float *dw = m == 0 ? p.g_w_out_proj : p.g_w_out_gate;
-  dw[o * kC + k] = acc * gam[k] + sv * bet[k];
+  const float *gam = m == 0 ? p.ln_x_w : p.ln_z_w;
+  const float *bet = m == 0 ? p.ln_x_b : p.ln_z_b;
+  float *dw = m == 0 ? p.g_w_y : p.g_w_t;
+  const float v = acc * gam[k] + sv * bet[k];
+  dw[o * kC + k] = p.grad_accumulate ? dw[o * kC + k] + v : v;
 }
 
 // LayerNorm parameter gradients: dgamma[k] = sum_o W[o][k] G[o][k],
-// dbeta[k] = sum_o W[o][k] S[o]; work-group m as above, thread k.
+// dbeta[k] = sum_o W[o][k] S[o] (W_y with G, S for LN_x; W_t with H, T for
+// LN_z).  Epilogue mode: work-group m = 0 writes LN_x's, m = 1 LN_z's.
+// Projection mode (LN_x = LN_z): one work-group writes the sum of both.
 template <typename T>
 __device__ __forceinline__ float elt(const T *w, int i);
 template <>
@@ -594,41 +636,51 @@ template <>
 __device__ __forceinline__ float elt<float>(const float *w, int i) { return w[i]; }
 
 template <typename T>
-__global__ __launch_bounds__(kC) void k3b_ln_grads(K3BArgs p) {
-  const int m = blockIdx.x, k = threadIdx.x;
-  const T *W = static_cast<const T *>(m == 0 ? p.w_out_proj : p.w_out_gate);
+__device__ __forceinline__ void ln_sums(const K3BArgs &p, int m, int k, float &dg, float &db) {
+  const T *W = static_cast<const T *>(m == 0 ? p.w_y : p.w_t);
   const float *Gt = p.tot + m * kC * kC;
   const float *St = p.tot + 2 * kC * kC + m * kC;
-  float dg = 0.f, db = 0.f;
   for (int o = 0; o < kC; ++o) {
     const float w = elt<T>(W, o * kC + k);
     dg += w * Gt[o * kC + k];
     db += w * St[o];
   }
-  (m == 0 ? p.g_ln_out_w : p.g_ln_in_w)[k] = dg;
-  (m == 0 ? p.g_ln_out_b : p.g_ln_in_b)[k] = db;
+}
+
+template <typename T, bool kProj>
+__global__ __launch_bounds__(kC) void k3b_ln_grads(K3BArgs p) {
+  const int m = blockIdx.x, k = threadIdx.x;
+  float dg = 0.f, db = 0.f;
+  ln_sums<T>(p, m, k, dg, db);
+  if constexpr (kProj) ln_sums<T>(p, 1, k, dg, db);
+  float *gw = (m == 0 && !kProj) ? p.g_ln_x_w : p.g_ln_z_w;
+  float *gb = (m == 0 && !kProj) ? p.g_ln_x_b : p.g_ln_z_b;
+  gw[k] = p.ln_accumulate ? gw[k] + dg : dg;
+  gb[k] = p.ln_accumulate ? gb[k] + db : db;
+}
+
+template <typename T, bool kProj>
+void launch_all(const K3BArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k3b_transpose<T>, dim3(2), dim3(256), 0, s, static_cast<const T *>(a.w_y),
+                     static_cast<const T *>(a.w_t), static_cast<T *>(a.wt));
+  hipLaunchKernelGGL((k3b_epilogue_grad<T, kProj>), dim3(a.n_parts), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(k3b_reduce, dim3(2 * kC), dim3(kC), 0, s, a);
+  hipLaunchKernelGGL((k3b_ln_grads<T, kProj>), dim3(kProj ? 1 : 2), dim3(kC), 0, s, a);
 }
 
 }  // namespace
 
-hipError_t launch_k3b(K3BArgs a, int dtype, hipStream_t s) {
+hipError_t launch_k3b(K3BArgs a, int dtype, bool projection, hipStream_t s) {
   const int64_t n_tiles = ((a.n_rows + 3) / 4) * ((a.n_cols + kCols - 1) / kCols);
   const int64_t slots = device_cu_count() < kK3BMaxParts ? device_cu_count() : kK3BMaxParts;
   a.n_parts = (int32_t)(n_tiles < slots ? (n_tiles > 0 ? n_tiles : 1) : slots);
   if (dtype == TRIMUL_BF16) {
-    hipLaunchKernelGGL(k3b_transpose<bf16_t>, dim3(2), dim3(256), 0, s, static_cast<const bf16_t *>(a.w_out_proj),
-                       static_cast<const bf16_t *>(a.w_out_gate), static_cast<bf16_t *>(a.wt));
-    hipLaunchKernelGGL(k3b_epilogue_grad<bf16_t>, dim3(a.n_parts), dim3(kThreads), 0, s, a);
+    if (projection) launch_all<bf16_t, true>(a, s);
+    else launch_all<bf16_t, false>(a, s);
   } else {
-    hipLaunchKernelGGL(k3b_transpose<float>, dim3(2), dim3(256), 0, s, static_cast<const float *>(a.w_out_proj),
-                       static_cast<const float *>(a.w_out_gate), static_cast<float *>(a.wt));
-    hipLaunchKernelGGL(k3b_epilogue_grad<float>, dim3(a.n_parts), dim3(kThreads), 0, s, a);
+    if (projection) launch_all<float, true>(a, s);
+    else launch_all<float, false>(a, s);
   }
-  hipLaunchKernelGGL(k3b_reduce, dim3(2 * kC), dim3(kC), 0, s, a);
-  if (dtype == TRIMUL_BF16)
-    hipLaunchKernelGGL(k3b_ln_grads<bf16_t>, dim3(2), dim3(kC), 0, s, a);
-  else
-    hipLaunchKernelGGL(k3b_ln_grads<float>, dim3(2), dim3(kC), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 //                        + pair mask, fp32 output
 //   KB (kb_relayout.hip) layout copies and transposes for the contraction's
 //                        gradients
-//   K3B (k3b_epilogue_grad.hip) backward of the epilogue: dL/dx, the gate
-//                        path's dL/dz and the epilogue's parameter gradients
+//   K3B (k3b_epilogue_grad.hip) backward of the epilogue (dL/dx, the gate
+//                        path's dL/dz, its parameter gradients) and of the
+//                        projections (their dL/dz and parameter gradients)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,25 +84,34 @@ struct RelayoutArgs {
   int64_t ld_q;           // >= round_up(rows, 64); columns rows .. round_up(rows, 64) get zeros
 };
 
-// K3B (k3b_epilogue_grad.hip): backward of the epilogue for a tile.
+// K3B (k3b_epilogue_grad.hip): backward of a gated, masked pair of 128 x 128
+// linear maps after LayerNorm, on a grid of n_rows x n_cols positions:
+//   out = m * sigmoid(W_t LN_z(z)) * (W_y LN_x(x))
+// Epilogue mode: x = the contraction result, W_y = W_out_proj, W_t =
+// W_out_gate, LN_x = the output LayerNorm, LN_z = the input LayerNorm.
+// Projection mode: x = z (LN_x = LN_z = the input LayerNorm), W_y / W_t = one
+// side's projection / gate matrices, out = that side's operand.
 struct K3BArgs {
-  const float *x;         // contraction result of the tile (x layout), as K3 reads it
-  int64_t ldx;
+  const float *x;         // epilogue: the contraction result (x layout, ldx)
+  int64_t ldx;            // row length of the x-layout buffers (x, dx; dout in projection mode)
   const void *z;          // [n][n][c_z] global
   const uint8_t *mask;    // [n][n] global
   int64_t n;
-  int64_t row_off, n_rows, col_off, n_cols;
-  const float *dout;      // [n_rows][n_cols][c_z] dL/dout
-  float *dx;              // dL/dx, x layout (may be x itself)
-  float *dz;              // [n_rows][n_cols][c_z] the gate path's share of dL/dz
-  const float *ln_out_w, *ln_out_b, *ln_in_w, *ln_in_b;
+  int64_t row_off, n_rows, col_off, n_cols;   // position (r, c) is pair (row_off + r, col_off + c),
+  int32_t transposed;                         // or (col_off + c, row_off + r) when transposed
+  int32_t grad_accumulate;                    // matrix gradients: 1 add, 0 overwrite
+  int32_t ln_accumulate;                      // LayerNorm-parameter gradients: 1 add, 0 overwrite
+  const float *dout;      // dL/dout: epilogue [n_rows][n_cols][c_z]; projection x layout (ldx)
+  float *dx;              // epilogue: dL/dx, x layout (may be x itself)
+  float *dz;              // epilogue: [n_rows][n_cols][c_z] written; projection: [n][n][c_z] added to
+  const float *ln_x_w, *ln_x_b, *ln_z_w, *ln_z_b;
   float eps;
-  const void *w_out_proj, *w_out_gate;
-  void *wt;               // workspace: W_out_proj^T, W_out_gate^T (element type)
+  const void *w_y, *w_t;  // [128][128] in the element type
+  void *wt;               // workspace: W_y^T, W_t^T (element type)
   float *part;            // workspace: kK3BMaxParts slots of kK3BSlotFloats
   float *tot;             // workspace: one slot, the sums over all work-groups
   int32_t n_parts;        // work-groups (set by the launcher)
-  float *g_w_out_proj, *g_w_out_gate, *g_ln_out_w, *g_ln_out_b, *g_ln_in_w, *g_ln_in_b;
+  float *g_w_y, *g_w_t, *g_ln_x_w, *g_ln_x_b, *g_ln_z_w, *g_ln_z_b;   // projection: g_ln_x_* unused
 };
 // Slot of one work-group's partial sums: G [128][128], H [128][128], S [128], T [128].
 constexpr int kK3BSlotFloats = 2 * 128 * 128 + 2 * 128;
@@ -113,7 +123,7 @@ hipError_t launch_k1(const K1Args &a, int dtype, hipStream_t s);
 hipError_t launch_k2(K2Args a, int dtype, hipStream_t s);
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s);
 hipError_t launch_relayout(const RelayoutArgs &a, bool from_x, int dtype, hipStream_t s);
-hipError_t launch_k3b(K3BArgs a, int dtype, hipStream_t s);
+hipError_t launch_k3b(K3BArgs a, int dtype, bool projection, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

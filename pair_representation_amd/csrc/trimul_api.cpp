@@ -567,24 +567,109 @@ trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, i
   a.dout = dout;
   a.dx = dx;
   a.dz = dz;
-  a.ln_out_w = w->ln_out_w;
-  a.ln_out_b = w->ln_out_b;
-  a.ln_in_w = w->ln_in_w;
-  a.ln_in_b = w->ln_in_b;
+  a.ln_x_w = w->ln_out_w;
+  a.ln_x_b = w->ln_out_b;
+  a.ln_z_w = w->ln_in_w;
+  a.ln_z_b = w->ln_in_b;
   a.eps = w->ln_eps;
-  a.w_out_proj = w->w_out_proj;
-  a.w_out_gate = w->w_out_gate;
+  a.w_y = w->w_out_proj;
+  a.w_t = w->w_out_gate;
   a.wt = ws + L.wt_off;
   a.tot = reinterpret_cast<float *>(ws + L.tot_off);
   a.part = reinterpret_cast<float *>(ws + L.part_off);
-  a.g_w_out_proj = grads->w_out_proj;
-  a.g_w_out_gate = grads->w_out_gate;
-  a.g_ln_out_w = grads->ln_out_w;
-  a.g_ln_out_b = grads->ln_out_b;
-  a.g_ln_in_w = grads->ln_in_w;
-  a.g_ln_in_b = grads->ln_in_b;
-  const hipError_t e = trimul::launch_k3b(a, w->dtype, static_cast<hipStream_t>(stream));
+  a.g_w_y = grads->w_out_proj;
+  a.g_w_t = grads->w_out_gate;
+  a.g_ln_x_w = grads->ln_out_w;
+  a.g_ln_x_b = grads->ln_out_b;
+  a.g_ln_z_w = grads->ln_in_w;
+  a.g_ln_z_b = grads->ln_in_b;
+  const hipError_t e = trimul::launch_k3b(a, w->dtype, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "epilogue backward kernel launch");
+  return ok();
+}
+
+size_t trimul_tile_operands_backward_workspace_bytes(const trimul_weights_t *w) {
+  return trimul_epilogue_backward_workspace_bytes(w);
+}
+
+trimul_status_t trimul_tile_operands_backward(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                              const uint8_t *mask, int64_t n, int64_t row_off, int64_t n_rows,
+                                              int64_t col_off, int64_t n_cols, int64_t k_off, int64_t k_len,
+                                              const float *da, const float *db, float *dz, uint32_t flags,
+                                              const trimul_projection_grads_t *grads, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING) return fail(TRIMUL_ERR_INVALID_ARG, "unknown direction %d", (int)dir);
+  if (n < 1 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [1, %lld]", (long long)n, (long long)kMaxN);
+  if (!da && !db) return fail(TRIMUL_ERR_INVALID_ARG, "da and db are both NULL");
+  if (da && (row_off < 0 || n_rows < 1 || row_off + n_rows > n))
+    return fail(TRIMUL_ERR_INVALID_ARG, "row range [%lld, +%lld) outside [0, %lld)", (long long)row_off, (long long)n_rows, (long long)n);
+  if (db && (col_off < 0 || n_cols < 1 || col_off + n_cols > n))
+    return fail(TRIMUL_ERR_INVALID_ARG, "col range [%lld, +%lld) outside [0, %lld)", (long long)col_off, (long long)n_cols, (long long)n);
+  if (k_off < 0 || k_len < 1 || k_off + k_len > n)
+    return fail(TRIMUL_ERR_INVALID_ARG, "k range [%lld, +%lld) outside [0, %lld)", (long long)k_off, (long long)k_len, (long long)n);
+  if (flags & ~(uint32_t)TRIMUL_GRAD_ACCUMULATE) return fail(TRIMUL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (!z || !mask || !dz) return fail(TRIMUL_ERR_INVALID_ARG, "z, mask and dz are required");
+  if (!aligned(z, 16) || !aligned(dz, 16) || (da && !aligned(da, 16)) || (db && !aligned(db, 16)))
+    return fail(TRIMUL_ERR_ALIGNMENT, "z, dz, da and db must be 16-byte aligned");
+  if (!grads) return fail(TRIMUL_ERR_INVALID_ARG, "grads is NULL");
+  struct Need {
+    bool on;
+    float *ptr;
+    const char *name;
+  } need[] = {{da != nullptr, grads->w_a_proj, "w_a_proj"}, {da != nullptr, grads->w_a_gate, "w_a_gate"},
+              {db != nullptr, grads->w_b_proj, "w_b_proj"}, {db != nullptr, grads->w_b_gate, "w_b_gate"},
+              {true, grads->ln_in_w, "ln_in_w"}, {true, grads->ln_in_b, "ln_in_b"}};
+  for (const Need &nd : need) {
+    if (!nd.on) continue;
+    if (!nd.ptr) return fail(TRIMUL_ERR_INVALID_ARG, "gradient %s is NULL", nd.name);
+    if (!aligned(nd.ptr, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "gradient %s is not 16-byte aligned", nd.name);
+  }
+  const EpilogueBackwardLayout L = epilogue_backward_layout(w->dtype);
+  if (!workspace) return fail(TRIMUL_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool accumulate = (flags & TRIMUL_GRAD_ACCUMULATE) != 0;
+  bool ln_accumulate = accumulate;
+  for (int side = 0; side < 2; ++side) {
+    const float *d = side == 0 ? da : db;
+    if (!d) continue;
+    trimul::K3BArgs a{};
+    a.ldx = x_ld(k_len);
+    a.z = z;
+    a.mask = mask;
+    a.n = n;
+    a.row_off = side == 0 ? row_off : col_off;   // plane row r <-> residue row_off + r (col_off + s for b)
+    a.n_rows = side == 0 ? n_rows : n_cols;
+    a.col_off = k_off;                           // plane column t <-> residue k_off + t
+    a.n_cols = k_len;
+    a.transposed = dir == TRIMUL_INCOMING;       // incoming operands are stored transposed
+    a.grad_accumulate = accumulate;
+    a.ln_accumulate = ln_accumulate;
+    a.dout = d;
+    a.dz = dz;
+    a.ln_x_w = a.ln_z_w = w->ln_in_w;
+    a.ln_x_b = a.ln_z_b = w->ln_in_b;
+    a.eps = w->ln_eps;
+    a.w_y = side == 0 ? w->w_a_proj : w->w_b_proj;
+    a.w_t = side == 0 ? w->w_a_gate : w->w_b_gate;
+    a.wt = ws + L.wt_off;
+    a.tot = reinterpret_cast<float *>(ws + L.tot_off);
+    a.part = reinterpret_cast<float *>(ws + L.part_off);
+    a.g_w_y = side == 0 ? grads->w_a_proj : grads->w_b_proj;
+    a.g_w_t = side == 0 ? grads->w_a_gate : grads->w_b_gate;
+    a.g_ln_z_w = grads->ln_in_w;
+    a.g_ln_z_b = grads->ln_in_b;
+    const hipError_t e = trimul::launch_k3b(a, w->dtype, true, s);
+    if (e != hipSuccess) return hip_fail(e, "projection backward kernel launch");
+    // the second side adds its input-LayerNorm share to the first's
+    ln_accumulate = true;
+  }
   return ok();
 }
 

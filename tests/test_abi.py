@@ -296,6 +296,54 @@ def test_epilogue_backward_validation():
     assert str(need) in L.trimul_last_error().decode()
 
 
+def call_pbwd(w=None, direction=pra.OUTGOING, n=100, row_off=10, n_rows=50, col_off=20, n_cols=40, k_off=5,
+              k_len=60, z=FAKE, mask=FAKE + 0x1000000, da=FAKE + 0x2000000, db=FAKE + 0x3000000,
+              dz=FAKE + 0x4000000, flags=0, grads="ok", null_grad=None, misalign_grad=None, ws=FAKE + 0x8000000,
+              ws_bytes=None):
+    L = pra.lib()
+    w = weights() if w is None else w
+    g = pra._ProjectionGrads(*[FAKE + 0x6000000 + 0x10000 * i for i in range(6)])
+    if null_grad:
+        setattr(g, null_grad, None)
+    if misalign_grad:
+        setattr(g, misalign_grad, FAKE + 0x6800000 + 4)
+    gp = ctypes.byref(g) if grads == "ok" else None
+    if ws_bytes is None:
+        ws_bytes = L.trimul_tile_operands_backward_workspace_bytes(ctypes.byref(w))
+    return L.trimul_tile_operands_backward(ctypes.byref(w), direction, z, mask, n, row_off, n_rows, col_off, n_cols,
+                                           k_off, k_len, da, db, dz, flags, gp, ws, ws_bytes, None)
+
+
+def test_tile_operands_backward_workspace_and_validation():
+    L = pra.lib()
+    for dt in (pra.BF16, pra.F32):
+        assert (L.trimul_tile_operands_backward_workspace_bytes(ctypes.byref(weights(dt)))
+                == L.trimul_epilogue_backward_workspace_bytes(ctypes.byref(weights(dt))))
+    assert call_pbwd(w=weights(c=64)) == pra.ERR_UNSUPPORTED
+    assert call_pbwd(direction=2) == pra.ERR_INVALID_ARG
+    assert call_pbwd(n=0) == pra.ERR_INVALID_ARG
+    assert call_pbwd(da=None, db=None) == pra.ERR_INVALID_ARG
+    assert call_pbwd(row_off=60) == pra.ERR_INVALID_ARG                 # a rows past n
+    assert call_pbwd(col_off=70) == pra.ERR_INVALID_ARG                 # b rows past n
+    assert call_pbwd(k_off=50, k_len=60) == pra.ERR_INVALID_ARG         # k past n
+    assert call_pbwd(k_len=0) == pra.ERR_INVALID_ARG
+    assert call_pbwd(flags=4) == pra.ERR_INVALID_ARG
+    for name in ("z", "mask", "dz"):
+        assert call_pbwd(**{name: None}) == pra.ERR_INVALID_ARG, name
+    for name in ("z", "dz", "da", "db"):
+        assert call_pbwd(**{name: FAKE + 0x9000000 + 8}) == pra.ERR_ALIGNMENT, name
+    assert call_pbwd(grads=None) == pra.ERR_INVALID_ARG
+    for name in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate", "ln_in_w", "ln_in_b"):
+        assert call_pbwd(null_grad=name) == pra.ERR_INVALID_ARG, name
+        assert call_pbwd(misalign_grad=name) == pra.ERR_ALIGNMENT, name
+    # a side that is not computed needs neither its rows nor its gradients
+    assert call_pbwd(da=None, row_off=90, null_grad="w_a_proj", ws=None) == pra.ERR_INVALID_ARG   # fails on ws only
+    assert "workspace" in L.trimul_last_error().decode()
+    assert call_pbwd(ws=FAKE + 0x40) == pra.ERR_ALIGNMENT
+    need = L.trimul_tile_operands_backward_workspace_bytes(ctypes.byref(weights()))
+    assert call_pbwd(ws_bytes=need - 1) == pra.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_status_strings():
     L = pra.lib()
     for s in range(6):

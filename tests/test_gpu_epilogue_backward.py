@@ -2,17 +2,18 @@
 the oracle's gradients (oracle.finish_vjp), through the C ABI.
 
 The inputs are exact in the storage dtype (z and the two matrices bf16 in bf16
-mode) and the oracle gets those exact values.  Every product on the matrix
-cores keeps fp32-level accuracy: in bf16 mode each non-weight operand is split
-into hi = bf16(v) and lo = bf16(v - hi) (representation error <= 2^-18 |v|)
-and the lo*lo term is dropped, so one product is off by at most about
-3 * 2^-18 = 1.1e-5 of its size; accumulation is fp32.  Bars, as
-max |diff| / rms(ref):
-  dx, dz (each entry a short sum of such products)         1e-4
+mode) and the oracle gets those exact values.  In bf16 mode each non-weight
+operand of a matrix-core product is split into hi = bf16(v) and
+lo = bf16(v - hi) (|v - hi| <= 2^-8 |v|, so the pair represents v to within
+2^-16 |v|) and the lo*lo term is dropped: one product is off by at most about
+3 * 2^-16 = 4.6e-5 of its size, and typically far less; accumulation is fp32.
+Bars, as max |diff| / rms(ref):
+  dx, dz (each entry a sum of 128 such products)           1e-4
   parameter gradients                                      3e-4
 the latter because a gradient summed over few pairs is close to a rank-1
 outer product, whose largest entries are 10-25 times its rms, and each entry
-carries the per-product relative error.  fp32 mode is well inside both.
+carries its product's relative error (measured: 1.0e-4 for one pair, under
+5e-5 otherwise).  fp32 mode is well inside both.
 
 x_acc is filled with NaN outside the tile's pairs: the padding of the
 accumulator layout must never reach a gradient.
