@@ -329,6 +329,86 @@ def bench_epilogue_backward(work, args, dev):
     return rec
 
 
+def bench_layer_backward(work, args, dev):
+    """The whole layer's backward on the N x N grid as one tile and one
+    k-chunk, from a forward run once (operands a, b and the contraction
+    result x kept) and a seeded N(0,1) dL/dout: epilogue backward (dL/dx, the
+    gate's dL/dz, its parameters), contraction backward (dL/da, dL/db) and
+    both projection sides (their dL/dz added, their parameters), timed per part
+    with HIP events on the launch stream.  The rate counts the N^2 pairs per
+    backward pass; the roofline line is the contraction backward's (its two
+    matrix-core contractions, 4 N^3 c flop), the dominant part."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    n = work.n
+    log(f"[bench] generating {work.name} (N={n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    kp = (n + 63) // 64 * 64
+    a_pl, b_pl = pra.tile_operands(w, pra.OUTGOING, z, mask, 0, n, 0, n, 0, n, kp)
+    x = pra.new_xacc(n, n, dev)
+    pra.tile(w, n, 0, n, 0, n, [(0, n, a_pl, b_pl)], pra.TILE_FIRST, x)
+    chunks = [(0, n, a_pl, b_pl)]
+    g = torch.Generator(device=dev).manual_seed(34567)
+    dout = torch.randn((n, n, C_Z), generator=g, device=dev)
+    dx = pra.new_xacc(n, n, dev)
+    dz = torch.empty((n, n, C_Z), dtype=torch.float32, device=dev)
+    da, db = [pra.new_xacc(n, n, dev)], [pra.new_xacc(n, n, dev)]
+    g_epi = {k: torch.empty(shp, dtype=torch.float32, device=dev) for k, shp in pra.EPILOGUE_GRAD_SHAPES.items()}
+    g_proj = {k: torch.empty(shp, dtype=torch.float32, device=dev) for k, shp in pra.PROJECTION_GRAD_SHAPES.items()}
+    g_proj["ln_in_w"], g_proj["ln_in_b"] = g_epi["ln_in_w"], g_epi["ln_in_b"]
+    ws_e = torch.empty(pra.epilogue_backward_workspace_bytes(w), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(pra.tile_backward_workspace_bytes(w, n, n, chunks), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pra.epilogue_backward(w, n, 0, n, 0, n, x, z, mask, dout, dx, dz, g_epi, ws_e)
+        if ev is not None:
+            ev[1].record()
+        pra.tile_backward(w, n, n, chunks, dx, da, db, ws_c)
+        if ev is not None:
+            ev[2].record()
+        for k in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate"):
+            g_proj[k].zero_()
+        pra.tile_operands_backward(w, pra.OUTGOING, z, mask, 0, n, 0, n, 0, n, da=da[0], db=db[0], dz=dz,
+                                   grads=g_proj, accumulate=True, workspace=ws_e)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} layer-backward passes")
+    evs = []
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    parts = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / len(evs) * 1e-3 for i in range(3)]
+    t = sum(parts)
+    flops = 4.0 * n * n * n * C
+    return {
+        "metric": "TriMul layer-backward pairs/s (all gradients: z and the ten parameters) at N=3605, c=128 bf16 "
+                  "(1 GPU)",
+        "value": n * n / t, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": work.dtype, "data": "synthetic (forward on the workload's seeded z; seeded N(0,1) dL/dout)",
+        "config": {"workload": work.name, "n": n, "part": "whole-layer backward, one tile, one chunk"},
+        "parts_ms": {"epilogue_backward": parts[0] * 1e3, "contraction_backward": parts[1] * 1e3,
+                     "projection_backward": parts[2] * 1e3},
+        "roofline": {"bound": "mfma", "kernel": "contraction backward (relayouts + two contractions)",
+                     "achieved": flops / parts[1] / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / parts[1] / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_per_launch": f"4*N^3*c = {flops:.4e} flop", "avg_launch_ms": parts[1] * 1e3},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
     """oracle.finish_vjp (numpy float64 on the host cores) on ``blocks``
     blocks of ``block`` seeded pairs, extrapolated to the N^2 pairs."""
@@ -361,10 +441,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "backward", "epilogue-backward"],
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "copy", "backward", "epilogue-backward", "layer-backward"],
                     help="copy: run a plain device copy of known size (HBM counter calibration); "
                          "backward: the contraction step's gradients (trimul_tile_backward); "
-                         "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward)")
+                         "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward); "
+                         "layer-backward: every gradient of the layer (the three backward entry points)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -394,6 +476,9 @@ def main():
         return
     if args.mode == "epilogue-backward":
         print(json.dumps(bench_epilogue_backward(work, args, dev)), flush=True)
+        return
+    if args.mode == "layer-backward":
+        print(json.dumps(bench_layer_backward(work, args, dev)), flush=True)
         return
     if work.tile:
         print(json.dumps(bench_tile(work, args, dev)), flush=True)
