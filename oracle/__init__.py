@@ -24,10 +24,12 @@ trimul_ref   vectorised float64 definition, Q-mode (bf16 contraction operands),
              blockwise and sampled evaluation, tile partial sums, and the
              gradients of the projections, the contraction step, the
              epilogue and the whole layer.
-bruteforce   per-element scalar loops of the same definition, for tiny inputs.
+bruteforce   per-element scalar loops of the same definitions, for tiny inputs.
+atom_attention  window-batched sequence-local atom attention (32-query blocks,
+             128-key windows; page 1, "Atom sequence local attention eficiente").
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle.py`` (brute force, closed forms, invariants, library
+``tests/test_oracle.py`` and ``tests/test_oracle_atom.py`` (brute force, closed forms, invariants, library
 special cases).  No function is "parity unpinned".
 """
 

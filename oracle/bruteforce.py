@@ -101,3 +101,42 @@ def contract_vjp_loops(a_rows, b_rows, dx):
                     da[i][k][d] += g * b_rows[j][k][d]
                     db[j][k][d] += g * a_rows[i][k][d]
     return da, db
+
+
+def window_attention_loops(q, k, v, bias=None, mask=None, scale=None):
+    """Scalar-loop spelling of ``atom_attention.window_attention`` (same
+    readings: query block i // 32, keys 32*(i // 32) - 48 .. + 127 that lie in
+    the sequence and are unmasked, softmax of scale * q.k + bias, 0 when no key
+    is left).  q, k, v are nested lists or arrays [batch][n][heads][d]."""
+    bsz, n, heads, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = [[[[0.0] * d for _ in range(heads)] for _ in range(n)] for _ in range(bsz)]
+    for b in range(bsz):
+        for i in range(n):
+            w = i // 32
+            first = 32 * w - 48
+            for h in range(heads):
+                logits = []
+                for t in range(128):
+                    j = first + t
+                    if j < 0 or j >= n or (mask is not None and mask[b][j] == 0):
+                        continue
+                    s = 0.0
+                    for e in range(d):
+                        s += float(q[b][i][h][e]) * float(k[b][j][h][e])
+                    s *= scale
+                    if bias is not None:
+                        s += float(bias[b][w][h][i - 32 * w][t])
+                    logits.append((j, s))
+                if not logits:
+                    continue
+                top = max(s for _, s in logits)
+                den = 0.0
+                for _, s in logits:
+                    den += math.exp(s - top)
+                for j, s in logits:
+                    p = math.exp(s - top) / den
+                    for e in range(d):
+                        out[b][i][h][e] += p * float(v[b][j][h][e])
+    return out
