@@ -409,6 +409,83 @@ def bench_layer_backward(work, args, dev):
     }
 
 
+ATOM_WORKLOAD = {"name": "atoms_b8_n28840_h4", "batch": 8, "n_atoms": 28840, "heads": 4, "keep": 0.9}
+
+
+def bench_atom_attention(args, dev):
+    """Window-batched atom attention (trimul_atom_window_attention) on 8
+    sequences of 28840 atoms (8 atoms per residue of the 3605-residue
+    workload), 4 heads of 32, a bf16 pair bias per window and 90% of the atoms
+    kept, timed with HIP events on the launch stream.  The rate counts
+    query-atom outputs (all heads) per second; the roofline is HBM: q, k, v
+    and the mask read once, the bias read once, the output written once (k
+    and v are read by four windows each, from L2)."""
+    import torch
+
+    import pair_representation_amd as pra
+
+    cfg = ATOM_WORKLOAD
+    bsz, n, heads = cfg["batch"], cfg["n_atoms"], cfg["heads"]
+    nw = (n + 31) // 32
+    g = torch.Generator(device=dev).manual_seed(45678)
+    q, k, v = (torch.randn((bsz, n, heads, 32), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    bias = torch.randn((bsz, nw, heads, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    mask = (torch.rand((bsz, n), generator=g, device=dev) < cfg["keep"]).to(torch.uint8)
+    out = torch.empty((bsz, n, heads, 32), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        pra.atom_window_attention(q, k, v, bias, mask, out=out)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        pra.atom_window_attention(q, k, v, bias, mask, out=out)
+        e[1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    t = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e-3
+    nbytes = float(3 * bsz * n * heads * 32 * 2 + bsz * nw * heads * 32 * 128 * 2 + bsz * n + bsz * n * heads * 32 * 4)
+    flops = 2.0 * 2 * bsz * nw * heads * 32 * 128 * 32
+    rec = {
+        "metric": "Atom window-attention query-atoms/s (32 x 128 windows, 4 heads of 32, pair bias) (1 GPU)",
+        "value": bsz * n / t, "unit": "query-atoms/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v and bias; 90% of atoms kept)",
+        "config": {"workload": cfg["name"], "batch": bsz, "n_atoms": n, "heads": heads, "head_dim": 32,
+                   "windows": f"{nw} x 32 queries x 128 keys per sequence"},
+        "roofline": {"bound": "hbm", "kernel": "ka_window_attention", "achieved": nbytes / t / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": nbytes / t / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_per_launch": f"{nbytes:.4e} B", "avg_launch_ms": t * 1e3,
+                     "matrix_core_TFLOP/s": flops / t / 1e12},
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        rec["cpu_baseline"] = cpu_baseline_atom_attention(cfg)
+    return rec
+
+
+def cpu_baseline_atom_attention(cfg, n_sample=28840):
+    """oracle.atom_attention.window_attention (numpy float64) on one seeded
+    sequence of n_sample atoms, extrapolated to the workload's query atoms."""
+    import numpy as np
+
+    from oracle import atom_attention as aa
+
+    r = np.random.default_rng(7)
+    heads = cfg["heads"]
+    q, k, v = (r.standard_normal((1, n_sample, heads, 32)) for _ in range(3))
+    bias = r.standard_normal((1, aa.n_windows(n_sample), heads, 32, 128))
+    mask = (r.random((1, n_sample)) < cfg["keep"]).astype(np.uint8)
+    t0 = time.perf_counter()
+    aa.window_attention(q, k, v, bias, mask)
+    dt = time.perf_counter() - t0
+    rate = n_sample / dt
+    total = cfg["batch"] * cfg["n_atoms"]
+    return {"value": rate, "unit": "query-atoms/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"oracle window_attention on one sequence of {n_sample} atoms ({dt:.2f}s); the "
+                      f"{total} query atoms of the workload would take {total / rate:.0f}s"}
+
+
 def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
     """oracle.finish_vjp (numpy float64 on the host cores) on ``blocks``
     blocks of ``block`` seeded pairs, extrapolated to the N^2 pairs."""
@@ -442,11 +519,12 @@ def main():
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "copy", "backward", "epilogue-backward", "layer-backward"],
+                    choices=["bench", "copy", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
                     help="copy: run a plain device copy of known size (HBM counter calibration); "
                          "backward: the contraction step's gradients (trimul_tile_backward); "
                          "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward); "
-                         "layer-backward: every gradient of the layer (the three backward entry points)")
+                         "layer-backward: every gradient of the layer (the three backward entry points); "
+                         "atom-attention: window-batched atom attention (trimul_atom_window_attention)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -469,6 +547,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
                           "launches": 3}), flush=True)
+        return
+    if args.mode == "atom-attention":
+        print(json.dumps(bench_atom_attention(args, dev)), flush=True)
         return
     work = wl.WORKLOADS[args.workload]
     if args.mode == "backward":

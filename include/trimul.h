@@ -320,6 +320,28 @@ trimul_status_t trimul_tile_operands_backward(const trimul_weights_t *w, trimul_
                                               const trimul_projection_grads_t *grads /* (host) */,
                                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Window-batched sequence-local atom attention (page 1, section "Atom sequence
+ * local attention eficiente": AlphaFold3 restricts atom attention to local
+ * windows of 32 x 128, processed as a batch of windows).  Per sequence b, the
+ * atoms are split into query blocks of 32 (block w = atoms 32w .. 32w+31, the
+ * last one possibly partial); block w attends to the 128 atoms centred on it,
+ * keys 32w - 48 .. 32w + 79, of which those inside the sequence and unmasked
+ * take part.  Per head h:
+ *   out_i = sum_j softmax_j(scale * q_i . k_j + bias[b][w][h][i - 32w][j - 32w + 48]) v_j
+ * and out_i = 0 for a query whose window has no key left.
+ *   q, k, v   : [batch][n_atoms][heads][head_dim] bf16, head_dim = 32
+ *   bias      : [batch][ceil(n_atoms / 32)][heads][32][128] bf16 (the pair
+ *               bias of each window: query row, key column), or NULL
+ *   atom_mask : [batch][n_atoms] uint8, nonzero keeps the atom as a key, or NULL
+ *   scale     : logit scale (1 / sqrt(head_dim) is the usual choice)
+ *   out       : [batch][n_atoms][heads][head_dim] fp32, fully overwritten
+ * Logits, softmax and accumulation are fp32; the probabilities enter the
+ * bf16 matrix-core product with V as two bf16 terms (hi + lo).  Needs no
+ * workspace. */
+trimul_status_t trimul_atom_window_attention(int64_t batch, int64_t n_atoms, int32_t heads, int32_t head_dim,
+                                             const void *q, const void *k, const void *v, const void *bias,
+                                             const uint8_t *atom_mask, float scale, float *out, void *stream);
+
 /* Static description of a status code. */
 const char *trimul_status_string(trimul_status_t s);
 

@@ -18,6 +18,7 @@ Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     epilogue_backward(w, n, row_off, n_rows, col_off, n_cols, x_acc, z, mask, dout, ...)
     tile_operands_backward_workspace_bytes(w)
     tile_operands_backward(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, da, db, dz, ...)
+    atom_window_attention(q, k, v, bias=None, atom_mask=None, scale=None, out=None)
 """
 
 from __future__ import annotations
@@ -125,6 +126,8 @@ def lib():
         L.trimul_tile_operands_backward.argtypes = [W, ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                                     vp, vp, vp, u32, ctypes.POINTER(_ProjectionGrads), vp, sz, vp]
         L.trimul_tile_operands_backward.restype = ctypes.c_int
+        L.trimul_atom_window_attention.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+        L.trimul_atom_window_attention.restype = ctypes.c_int
         L.trimul_status_string.argtypes = [ctypes.c_int]
         L.trimul_status_string.restype = ctypes.c_char_p
         L.trimul_last_error.argtypes = []
@@ -463,3 +466,30 @@ def tile_operands_backward(w: Weights, direction, z, mask, row_off, n_rows, col_
                                                GRAD_ACCUMULATE if accumulate else 0, ctypes.byref(g),
                                                _ptr(workspace), workspace.numel(), _stream()))
     return dz, grads
+
+
+def atom_window_attention(q, k, v, bias=None, atom_mask=None, scale=None, out=None):
+    """Window-batched sequence-local atom attention (32-atom query blocks, each
+    attending to the 128 atoms centred on it).  q, k, v: bf16 [batch, n_atoms,
+    heads, 32]; bias: bf16 [batch, ceil(n_atoms / 32), heads, 32, 128] or None;
+    atom_mask: uint8 [batch, n_atoms] or None (keys only); scale defaults to
+    1/sqrt(32).  Returns out, fp32 [batch, n_atoms, heads, 32]."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, n_atoms, heads, head_dim]")
+    bsz, n, heads, d = q.shape
+    _need(k, "k", torch.bfloat16, q.shape)
+    _need(v, "v", torch.bfloat16, q.shape)
+    nw = (n + 31) // 32
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, (bsz, nw, heads, 32, 128))
+    if atom_mask is not None:
+        _need(atom_mask, "atom_mask", torch.uint8, (bsz, n))
+    if out is None:
+        out = torch.empty((bsz, n, heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (bsz, n, heads, d))
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib().trimul_atom_window_attention(bsz, n, heads, d, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                              _ptr(atom_mask), float(scale), _ptr(out), _stream()))
+    return out

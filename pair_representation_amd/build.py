@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtrimul.so")
 
 SOURCES = ["k1_project.hip", "k2_contract.hip", "k3_epilogue.hip", "k3b_epilogue_grad.hip", "kb_relayout.hip",
-           "trimul_api.cpp"]
+           "ka_window_attention.hip", "trimul_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
 HIP_FLAGS = [

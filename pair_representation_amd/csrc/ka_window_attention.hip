@@ -1,0 +1,193 @@
+// KA: window-batched sequence-local atom attention (page 1, section "Atom
+// sequence local attention eficiente": AlphaFold3 restricts atom attention to
+// local windows of 32 x 128, processed as a batch of windows).
+//
+// Query block w = atoms 32w .. 32w+31 attends to the 128 atoms centred on it,
+// keys 32w - 48 .. 32w + 79 (those inside the sequence and not masked); per
+// head, o_i = softmax_j(scale q_i.k_j + bias_ij) v_j, o_i = 0 when no key is
+// left.  q, k, v are bf16 [batch][n][heads][32]; bias bf16
+// [batch][windows][heads][32][128] (optional); out fp32 [batch][n][heads][32].
+//
+// Work-group = one (sequence, window), 4 waves; wave v takes heads v, v+4, ...
+// Per head, on the matrix cores (bf16 32x32x16, fp32 accumulation):
+//  - S^T = K Q^T for the 4 key blocks of 32: lane l holds query l % 32 and 16
+//    keys of each block, so a query's 128 logits sit in two lanes (l, l ^ 32):
+//    the softmax needs an in-lane reduction plus one lane swap;
+//  - O = P V with the normalised probabilities as A operand straight from the
+//    S^T registers: key block b, step s takes accumulator registers 8s .. 8s+7
+//    of lane (q, half), i.e. keys 32b + 16s + 4 half + {0..3, 8..11}; the B
+//    operand reads the same keys of V from a transposed LDS copy (two 8-byte
+//    reads).  P is split into hi + lo bf16 terms (two products per step), so
+//    the output keeps about 16 significant bits of P.
+// Key validity (inside the sequence and unmasked) is computed once per
+// work-group into LDS.  Keys outside the sequence read a clamped row (finite
+// values) and get probability 0.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace trimul {
+
+namespace {
+
+constexpr int kQ = 32;          // queries per window
+constexpr int kK = 128;         // keys per window
+constexpr int kKOff = -48;      // first key relative to 32w
+constexpr int kD = 32;          // head dimension
+constexpr int kWaves = 4;
+constexpr int kVtStride = kK + 8;   // LDS row of V^T (bf16 elements): 272 bytes, spreads the d rows over banks
+
+__global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][kD * kVtStride];   // V^T per wave: [d][key]
+  __shared__ uint8_t key_ok[kK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wg = blockIdx.x;
+  const int64_t b = wg / p.n_windows, w = wg % p.n_windows;
+  const int64_t key0 = kQ * w + kKOff;
+  const int q = lane & 31, hl = lane >> 5;
+  const int64_t n = p.n_atoms;
+
+  if (threadIdx.x < kK) {
+    const int64_t j = key0 + threadIdx.x;
+    bool ok = j >= 0 && j < n;
+    if (ok && p.mask) ok = p.mask[b * n + j] != 0;
+    key_ok[threadIdx.x] = ok ? 1 : 0;
+  }
+  __syncthreads();
+
+  const bf16_t *Q = static_cast<const bf16_t *>(p.q);
+  const bf16_t *Kp = static_cast<const bf16_t *>(p.k);
+  const bf16_t *V = static_cast<const bf16_t *>(p.v);
+  const bf16_t *Bias = static_cast<const bf16_t *>(p.bias);
+  const int64_t H = p.heads;
+  // element offset of (atom j, head h, dim 0) of sequence b
+  auto row = [&](int64_t j, int64_t h) -> int64_t { return ((b * n + j) * H + h) * kD; };
+  auto clampj = [&](int64_t j) -> int64_t { return j < 0 ? 0 : (j >= n ? n - 1 : j); };
+  const float kLog2e = 1.4426950408889634f;
+  const float sl = p.scale * kLog2e;
+  uint16_t *const myvt = vt[wave];
+
+  // every wave runs the same number of rounds (the barriers below are
+  // reached by all of them); a wave whose head does not exist idles
+  for (int64_t h0 = 0; h0 < H; h0 += kWaves) {
+    const int64_t h = h0 + wave;
+    const bool act = h < H;
+    // ---- V^T of the window into LDS: lane -> key 16 it + l / 4, dims 8 (l % 4) .. +7
+#pragma unroll
+    for (int it = 0; act && it < kK / 16; ++it) {
+      const int t = 16 * it + (lane >> 2), c = lane & 3;
+      const u32x4 v4 = *reinterpret_cast<const u32x4 *>(V + row(clampj(key0 + t), h) + 8 * c);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        myvt[(8 * c + 2 * m) * kVtStride + t] = (uint16_t)(v4[m] & 0xffffu);
+        myvt[(8 * c + 2 * m + 1) * kVtStride + t] = (uint16_t)(v4[m] >> 16);
+      }
+    }
+    __syncthreads();   // V^T written (each wave reads only its own copy)
+    if (act) {
+    // ---- S^T = K Q^T: 4 key blocks x 2 steps over d ------------------------
+    Frag<bf16_t> qf[2];
+    const int64_t qi = kQ * w + q;
+    const int64_t qrow = row(qi < n ? qi : n - 1, h);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * hl);
+    f32x16 s[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[bb][e] = 0.f;
+      const int64_t krow = row(clampj(key0 + 32 * bb + q), h);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<bf16_t> kf;
+        kf.load(Kp + krow + 16 * ks + 8 * hl);
+        mma(s[bb], kf, qf[ks]);
+      }
+    }
+    // ---- logits (base-2 units), masked keys -> -inf; row max over 128 keys ---
+    const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + q) * kK : nullptr;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int t0 = 32 * bb + 8 * g + 4 * hl;   // keys t0 .. t0+3 of this lane
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (brow) {
+          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+          const u32x2 raw = *reinterpret_cast<const u32x2 *>(brow + t0);
+          bv[0] = __uint_as_float(raw[0] << 16);
+          bv[1] = __uint_as_float(raw[0] & 0xffff0000u);
+          bv[2] = __uint_as_float(raw[1] << 16);
+          bv[3] = __uint_as_float(raw[1] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          const float l2 = key_ok[t0 + i] ? s[bb][e] * sl + bv[i] * kLog2e : -__builtin_inff();
+          s[bb][e] = l2;
+          mx = fmaxf(mx, l2);
+        }
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // ---- probabilities; a query with no key gets p = 0 ---------------------
+    float sum = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = mx == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(s[bb][e] - mx);
+        s[bb][e] = pe;
+        sum += pe;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    // ---- O = P V over 8 steps of 16 keys (P split into hi + lo) -------------
+    f32x16 o;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 hh, ll;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f0 = s[bb][8 * st + 2 * i] * inv, f1 = s[bb][8 * st + 2 * i + 1] * inv;
+          hh[i] = pack_bf16x2(f0, f1);
+          ll[i] = pack_bf16x2(f0 - __uint_as_float(hh[i] << 16), f1 - __uint_as_float(hh[i] & 0xffff0000u));
+        }
+        Frag<bf16_t> ph, pl, vf;
+        ph.v = __builtin_bit_cast(bf16x8, hh);
+        pl.v = __builtin_bit_cast(bf16x8, ll);
+        // V at keys 32bb + 16st + 4hl + {0..3} and + 8 + {0..3}, dim q (this lane's column)
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+        const uint16_t *vr = myvt + q * kVtStride + 32 * bb + 16 * st + 4 * hl;
+        const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vr);
+        const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vr + 8);
+        vf.v = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        mma(o, ph, vf);
+        mma(o, pl, vf);
+      }
+    // ---- out[b][32w + row][h][d = lane % 32] ---------------------------------
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t oi = kQ * w + acc_row(e, lane);
+      if (oi < n) p.out[((b * n + oi) * H + h) * kD + q] = o[e];
+    }
+    }  // act
+    __syncthreads();   // this head's V^T reads are done before the next round overwrites it
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ka(const KAArgs &a, hipStream_t s) {
+  const int64_t grid = a.batch * a.n_windows;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ka_window_attention, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace trimul

@@ -10,6 +10,7 @@
 //   K3B (k3b_epilogue_grad.hip) backward of the epilogue (dL/dx, the gate
 //                        path's dL/dz, its parameter gradients) and of the
 //                        projections (their dL/dz and parameter gradients)
+//   KA (ka_window_attention.hip) window-batched atom attention (32 x 128)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -113,6 +114,16 @@ struct K3BArgs {
   int32_t n_parts;        // work-groups (set by the launcher)
   float *g_w_y, *g_w_t, *g_ln_x_w, *g_ln_x_b, *g_ln_z_w, *g_ln_z_b;   // projection: g_ln_x_* unused
 };
+// KA (ka_window_attention.hip): window-batched sequence-local atom attention.
+struct KAArgs {
+  const void *q, *k, *v;  // bf16 [batch][n_atoms][heads][32]
+  const void *bias;       // bf16 [batch][n_windows][heads][32][128] or null
+  const uint8_t *mask;    // [batch][n_atoms] (nonzero keeps the atom as a key) or null
+  float *out;             // fp32 [batch][n_atoms][heads][32]
+  int64_t batch, n_atoms, n_windows, heads;
+  float scale;            // logit scale
+};
+
 // Slot of one work-group's partial sums: G [128][128], H [128][128], S [128], T [128].
 constexpr int kK3BSlotFloats = 2 * 128 * 128 + 2 * 128;
 constexpr int kK3BMaxParts = 256;
@@ -124,6 +135,7 @@ hipError_t launch_k2(K2Args a, int dtype, hipStream_t s);
 hipError_t launch_k3(const K3Args &a, int dtype, hipStream_t s);
 hipError_t launch_relayout(const RelayoutArgs &a, bool from_x, int dtype, hipStream_t s);
 hipError_t launch_k3b(K3BArgs a, int dtype, bool projection, hipStream_t s);
+hipError_t launch_ka(const KAArgs &a, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

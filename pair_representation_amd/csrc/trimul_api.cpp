@@ -673,6 +673,36 @@ trimul_status_t trimul_tile_operands_backward(const trimul_weights_t *w, trimul_
   return ok();
 }
 
+trimul_status_t trimul_atom_window_attention(int64_t batch, int64_t n_atoms, int32_t heads, int32_t head_dim,
+                                             const void *q, const void *k, const void *v, const void *bias,
+                                             const uint8_t *atom_mask, float scale, float *out, void *stream) {
+  if (batch < 1 || n_atoms < 1) return fail(TRIMUL_ERR_INVALID_ARG, "batch=%lld n_atoms=%lld must be >= 1", (long long)batch, (long long)n_atoms);
+  if (head_dim != 32) return fail(TRIMUL_ERR_UNSUPPORTED, "head_dim=%d: only 32 is supported", head_dim);
+  if (heads < 1 || heads > 1024) return fail(TRIMUL_ERR_INVALID_ARG, "heads=%d outside [1, 1024]", heads);
+  const int64_t n_windows = (n_atoms + 31) / 32;
+  if (batch > (int64_t(1) << 40) / n_atoms || batch * n_windows > 0x7fffffff)
+    return fail(TRIMUL_ERR_INVALID_ARG, "batch * n_atoms too large");
+  if (!q || !k || !v || !out) return fail(TRIMUL_ERR_INVALID_ARG, "q, k, v and out are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || (bias && !aligned(bias, 16)))
+    return fail(TRIMUL_ERR_ALIGNMENT, "q, k, v, bias and out must be 16-byte aligned");
+  if (!(scale == scale) || scale > 1e30f || scale < -1e30f) return fail(TRIMUL_ERR_INVALID_ARG, "scale must be finite");
+  trimul::KAArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bias = bias;
+  a.mask = atom_mask;
+  a.out = out;
+  a.batch = batch;
+  a.n_atoms = n_atoms;
+  a.n_windows = n_windows;
+  a.heads = heads;
+  a.scale = scale;
+  const hipError_t e = trimul::launch_ka(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "window attention kernel launch");
+  return ok();
+}
+
 const char *trimul_status_string(trimul_status_t s) {
   switch (s) {
     case TRIMUL_OK: return "ok";

@@ -344,6 +344,26 @@ def test_tile_operands_backward_workspace_and_validation():
     assert call_pbwd(ws_bytes=need - 1) == pra.ERR_WORKSPACE_TOO_SMALL
 
 
+def call_attn(batch=2, n=100, heads=4, d=32, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, bias=None, mask=None,
+              scale=0.17, out=FAKE + 0x300000):
+    return pra.lib().trimul_atom_window_attention(batch, n, heads, d, q, k, v, bias, mask, scale, out, None)
+
+
+def test_atom_window_attention_validation():
+    assert call_attn(batch=0) == pra.ERR_INVALID_ARG
+    assert call_attn(n=0) == pra.ERR_INVALID_ARG
+    assert call_attn(d=64) == pra.ERR_UNSUPPORTED
+    assert call_attn(heads=0) == pra.ERR_INVALID_ARG
+    assert call_attn(heads=2000) == pra.ERR_INVALID_ARG
+    assert call_attn(batch=1 << 30, n=1 << 20) == pra.ERR_INVALID_ARG
+    for name in ("q", "k", "v", "out"):
+        assert call_attn(**{name: None}) == pra.ERR_INVALID_ARG, name
+        assert call_attn(**{name: FAKE + 0x400000 + 8}) == pra.ERR_ALIGNMENT, name
+    assert call_attn(bias=FAKE + 0x500000 + 4) == pra.ERR_ALIGNMENT
+    assert call_attn(scale=float("nan")) == pra.ERR_INVALID_ARG
+    assert call_attn(scale=float("inf")) == pra.ERR_INVALID_ARG
+
+
 def test_status_strings():
     L = pra.lib()
     for s in range(6):
