@@ -9,6 +9,9 @@
 // [batch][windows][heads][32][128] (optional); out fp32 [batch][n][heads][32].
 //
 // Work-group = one (sequence, window), 4 waves; wave v takes heads v, v+4, ...
+// (two waves per SIMD: the register budget is held to 256 per lane).  Per
+// head, all global loads (Q, K, the bias row, V) are issued before any use, so
+// a head costs one memory round trip.
 // Per head, on the matrix cores (bf16 32x32x16, fp32 accumulation):
 //  - S^T = K Q^T for the 4 key blocks of 32: lane l holds query l % 32 and 16
 //    keys of each block, so a query's 128 logits sit in two lanes (l, l ^ 32):
@@ -36,7 +39,7 @@ constexpr int kD = 32;          // head dimension
 constexpr int kWaves = 4;
 constexpr int kVtStride = kK + 8;   // LDS row of V^T (bf16 elements): 272 bytes, spreads the d rows over banks
 
-__global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void ka_window_attention(KAArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][kD * kVtStride];   // V^T per wave: [d][key]
   __shared__ uint8_t key_ok[kK];
 
@@ -68,14 +71,35 @@ __global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
   const float sl = p.scale * kLog2e;
   uint16_t *const myvt = vt[wave];
 
-  // every wave runs the same number of rounds (the barriers below are
-  // reached by all of them); a wave whose head does not exist idles
-  for (int64_t h0 = 0; h0 < H; h0 += kWaves) {
-    const int64_t h = h0 + wave;
-    const bool act = h < H;
-    // ---- V^T of the window into LDS: lane -> key 16 it + l / 4, dims 8 (l % 4) .. +7
+  // Each wave owns its V^T copy, so no work-group barrier is needed inside the
+  // loop: the wave's LDS operations execute in order, and compiler barriers
+  // keep the copy's writes before its reads and this head's reads before the
+  // next head's writes.  All global loads of a head are issued first.
+  for (int64_t h = wave; h < H; h += kWaves) {
+    // ---- loads: Q (B operand over d), K (A operand, 4 key blocks), bias, V
+    Frag<bf16_t> qf[2], kf[4][2];
+    const int64_t qi = kQ * w + q;
+    const int64_t qrow = row(qi < n ? qi : n - 1, h);
 #pragma unroll
-    for (int it = 0; act && it < kK / 16; ++it) {
+    for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * hl);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int64_t krow = row(clampj(key0 + 32 * bb + q), h);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) kf[bb][ks].load(Kp + krow + 16 * ks + 8 * hl);
+    }
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + q) * kK : nullptr;
+    u32x2 braw[4][4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        braw[bb][g] = brow ? *reinterpret_cast<const u32x2 *>(brow + 32 * bb + 8 * g + 4 * hl) : u32x2{0u, 0u};
+    // ---- V^T of the window into LDS: lane -> key 16 it + l / 4, dims 8 (l % 4) .. +7
+    asm volatile("" ::: "memory");   // the previous head's V^T reads stay before these writes
+#pragma unroll
+    for (int it = 0; it < kK / 16; ++it) {
       const int t = 16 * it + (lane >> 2), c = lane & 3;
       const u32x4 v4 = *reinterpret_cast<const u32x4 *>(V + row(clampj(key0 + t), h) + 8 * c);
 #pragma unroll
@@ -84,44 +108,26 @@ __global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
         myvt[(8 * c + 2 * m + 1) * kVtStride + t] = (uint16_t)(v4[m] >> 16);
       }
     }
-    __syncthreads();   // V^T written (each wave reads only its own copy)
-    if (act) {
+    asm volatile("" ::: "memory");   // the writes stay before the reads below
     // ---- S^T = K Q^T: 4 key blocks x 2 steps over d ------------------------
-    Frag<bf16_t> qf[2];
-    const int64_t qi = kQ * w + q;
-    const int64_t qrow = row(qi < n ? qi : n - 1, h);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * hl);
     f32x16 s[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[bb][e] = 0.f;
-      const int64_t krow = row(clampj(key0 + 32 * bb + q), h);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Frag<bf16_t> kf;
-        kf.load(Kp + krow + 16 * ks + 8 * hl);
-        mma(s[bb], kf, qf[ks]);
-      }
+      for (int ks = 0; ks < 2; ++ks) mma(s[bb], kf[bb][ks], qf[ks]);
     }
     // ---- logits (base-2 units), masked keys -> -inf; row max over 128 keys ---
-    const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + q) * kK : nullptr;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int t0 = 32 * bb + 8 * g + 4 * hl;   // keys t0 .. t0+3 of this lane
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (brow) {
-          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-          const u32x2 raw = *reinterpret_cast<const u32x2 *>(brow + t0);
-          bv[0] = __uint_as_float(raw[0] << 16);
-          bv[1] = __uint_as_float(raw[0] & 0xffff0000u);
-          bv[2] = __uint_as_float(raw[1] << 16);
-          bv[3] = __uint_as_float(raw[1] & 0xffff0000u);
-        }
+        const u32x2 raw = braw[bb][g];
+        const float bv[4] = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                             __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g + i;
@@ -162,7 +168,6 @@ __global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
         ph.v = __builtin_bit_cast(bf16x8, hh);
         pl.v = __builtin_bit_cast(bf16x8, ll);
         // V at keys 32bb + 16st + 4hl + {0..3} and + 8 + {0..3}, dim q (this lane's column)
-        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
         const uint16_t *vr = myvt + q * kVtStride + 32 * bb + 16 * st + 4 * hl;
         const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vr);
         const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vr + 8);
@@ -176,8 +181,6 @@ __global__ __launch_bounds__(64 * kWaves) void ka_window_attention(KAArgs p) {
       const int64_t oi = kQ * w + acc_row(e, lane);
       if (oi < n) p.out[((b * n + oi) * H + h) * kD + q] = o[e];
     }
-    }  // act
-    __syncthreads();   // this head's V^T reads are done before the next round overwrites it
   }
 }
 
