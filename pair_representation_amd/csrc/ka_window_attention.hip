@@ -16,12 +16,14 @@
 //  - S^T = K Q^T for the 4 key blocks of 32: lane l holds query l % 32 and 16
 //    keys of each block, so a query's 128 logits sit in two lanes (l, l ^ 32):
 //    the softmax needs an in-lane reduction plus one lane swap;
+//    Rows of a key block stand for permuted keys (kperm) so that lane (q, half)
+//    holds keys 16 half .. +15 of each block;
 //  - O = P V with the normalised probabilities as A operand straight from the
 //    S^T registers: key block b, step s takes accumulator registers 8s .. 8s+7
-//    of lane (q, half), i.e. keys 32b + 16s + 4 half + {0..3, 8..11}; the B
-//    operand reads the same keys of V from a transposed LDS copy (two 8-byte
-//    reads).  P is split into hi + lo bf16 terms (two products per step), so
-//    the output keeps about 16 significant bits of P.
+//    of lane (q, half), i.e. keys 32b + 16 half + 8s .. +7; the B operand reads
+//    the same keys of V from a transposed LDS copy (one 16-byte read).  P is
+//    split into hi + lo bf16 terms (two products per step), so the output
+//    keeps about 16 significant bits of P.
 // Key validity (inside the sequence and unmasked) is computed once per
 // work-group into LDS.  Keys outside the sequence read a clamped row (finite
 // values) and get probability 0.
@@ -49,6 +51,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t b = wg / p.n_windows, w = wg % p.n_windows;
   const int64_t key0 = kQ * w + kKOff;
   const int q = lane & 31, hl = lane >> 5;
+  // Row r of a 32-key block of S^T stands for key 16 ((r >> 2) & 1) + 4 (r >> 3)
+  // + (r & 3): the 16 rows a lane holds (acc_row(e, l), e = 0..15) are then
+  // keys 16 (l / 32) + e, so the lane's bias, key flags and V operands are
+  // contiguous runs.
+  const int kperm = 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
   const int64_t n = p.n_atoms;
 
   if (threadIdx.x < kK) {
@@ -84,18 +91,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * hl);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-      const int64_t krow = row(clampj(key0 + 32 * bb + q), h);
+      const int64_t krow = row(clampj(key0 + 32 * bb + kperm), h);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) kf[bb][ks].load(Kp + krow + 16 * ks + 8 * hl);
     }
-    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
     const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + q) * kK : nullptr;
-    u32x2 braw[4][4];
+    u32x4 braw[4][2];   // keys 32 bb + 16 hl + 8 j .. +7 of this lane's query
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        braw[bb][g] = brow ? *reinterpret_cast<const u32x2 *>(brow + 32 * bb + 8 * g + 4 * hl) : u32x2{0u, 0u};
+      for (int j = 0; j < 2; ++j)
+        braw[bb][j] = brow ? *reinterpret_cast<const u32x4 *>(brow + 32 * bb + 16 * hl + 8 * j) : u32x4{0u, 0u, 0u, 0u};
     // ---- V^T of the window into LDS: lane -> key 16 it + l / 4, dims 8 (l % 4) .. +7
     asm volatile("" ::: "memory");   // the previous head's V^T reads stay before these writes
 #pragma unroll
@@ -123,18 +129,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int t0 = 32 * bb + 8 * g + 4 * hl;   // keys t0 .. t0+3 of this lane
-        const u32x2 raw = braw[bb][g];
-        const float bv[4] = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
-                             __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g + i;
-          const float l2 = key_ok[t0 + i] ? s[bb][e] * sl + bv[i] * kLog2e : -__builtin_inff();
-          s[bb][e] = l2;
-          mx = fmaxf(mx, l2);
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int t = 32 * bb + 16 * hl + e;   // key of register e (see kperm)
+        const uint32_t word = braw[bb][e >> 3][(e & 7) >> 1];
+        const float bv = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+        const float l2 = key_ok[t] ? s[bb][e] * sl + bv * kLog2e : -__builtin_inff();
+        s[bb][e] = l2;
+        mx = fmaxf(mx, l2);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // ---- probabilities; a query with no key gets p = 0 ---------------------
@@ -167,11 +168,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
         Frag<bf16_t> ph, pl, vf;
         ph.v = __builtin_bit_cast(bf16x8, hh);
         pl.v = __builtin_bit_cast(bf16x8, ll);
-        // V at keys 32bb + 16st + 4hl + {0..3} and + 8 + {0..3}, dim q (this lane's column)
-        const uint16_t *vr = myvt + q * kVtStride + 32 * bb + 16 * st + 4 * hl;
-        const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vr);
-        const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vr + 8);
-        vf.v = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        // V at keys 32bb + 16hl + 8st .. +7 (registers 8st .. 8st+7 of the A
+        // lanes with this half), dim q (this lane's column)
+        vf.v = *reinterpret_cast<const bf16x8 *>(myvt + q * kVtStride + 32 * bb + 16 * hl + 8 * st);
         mma(o, ph, vf);
         mma(o, pl, vf);
       }
