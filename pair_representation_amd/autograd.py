@@ -17,6 +17,7 @@ operands a, b and the contraction result x for the backward (in bf16 mode
 from __future__ import annotations
 
 import torch
+from torch.autograd.function import once_differentiable
 
 from . import (BF16, F32, INCOMING, OUTGOING, TILE_FIRST, TILE_LAST, Weights, epilogue_backward, new_xacc, tile,
                tile_backward, tile_operands, tile_operands_backward)
@@ -45,12 +46,14 @@ class TriMul(torch.autograd.Function):
         return out
 
     @staticmethod
+    @once_differentiable
     def backward(ctx, dout):
         z, mask, x, a, b, *params = ctx.saved_tensors
         w = Weights(dict(zip(PARAM_NAMES, params)), ctx.dtype, eps=ctx.eps, device=z.device)
         n = z.shape[0]
-        # dx over x (each pair's x is read before its dx is written)
-        dx, dz, g_epi = epilogue_backward(w, n, 0, n, 0, n, x, z, mask, dout.contiguous().float(), dx=x)
+        # dx in a buffer of its own: the saved x stays intact for a second
+        # backward through the same graph (retain_graph)
+        dx, dz, g_epi = epilogue_backward(w, n, 0, n, 0, n, x, z, mask, dout.contiguous().float())
         da, db = tile_backward(w, n, n, [(0, n, a, b)], dx)
         g_proj = {k: torch.zeros(params[PARAM_NAMES.index(k)].shape, dtype=torch.float32, device=z.device)
                   for k in ("w_a_proj", "w_a_gate", "w_b_proj", "w_b_gate")}

@@ -173,3 +173,24 @@ def test_layer_autograd_matches_oracle(dev, dtype, direction, n):
     print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
         assert v <= tol[k], (k, v)
+
+
+def test_layer_autograd_second_backward_is_identical(dev):
+    """Two backward passes through one graph (retain_graph) give the same
+    gradients: the backward leaves the saved forward state untouched."""
+    print("[case] layer autograd twice", flush=True)
+    n = 45
+    z, mask, wts = wl.make_small(n, seed=77, dtype="bf16", device="cpu")
+    params = _params(wts, dev)
+    zd = z.to(dev).requires_grad_(True)
+    out = pag.trimul(zd, mask.to(dev), params, pra.OUTGOING)
+    g = torch.randn_like(out)
+    out.backward(g, retain_graph=True)
+    first = [zd.grad.clone()] + [params[k].grad.clone() for k in pag.PARAM_NAMES]
+    for t in [zd] + [params[k] for k in pag.PARAM_NAMES]:
+        t.grad = None
+    out.backward(g)
+    second = [zd.grad] + [params[k].grad for k in pag.PARAM_NAMES]
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
