@@ -74,7 +74,8 @@ typedef enum { TRIMUL_OUTGOING = 0, TRIMUL_INCOMING = 1 } trimul_dir_t;
 
 /* Flags of trimul_tile. */
 enum { TRIMUL_TILE_FIRST = 1u, TRIMUL_TILE_LAST = 2u };
-/* Flag of trimul_tile_operands_backward: add the parameter gradients to the
+/* Flag of the backward entry points that produce parameter gradients
+ * (trimul_epilogue_backward, trimul_tile_operands_backward): add them to the
  * grads buffers instead of overwriting them. */
 enum { TRIMUL_GRAD_ACCUMULATE = 1u };
 
@@ -252,7 +253,8 @@ typedef struct {
  *   dz     = [n_rows][n_cols][c_z] fp32: the output gate's share of
  *            dL/dz_(row_off+r, col_off+s) (through ln_in and W_out_gate; the
  *            a/b projections contribute the rest)
- *   grads  = sums over the tile's pairs (masked pairs contribute nothing; a
+ *   grads  = sums over the tile's pairs (masked pairs contribute nothing),
+ *            overwritten, or added to with flags = TRIMUL_GRAD_ACCUMULATE (a
  *            layer split into tiles sums the tiles' results)
  * Masked pairs get dx = dz = 0.  The weight-matrix gradients are formed as
  * dW_out_proj = G diag(ln_out_w) + S ln_out_b^T with G = sum dy LN0(x)^T and
@@ -270,7 +272,7 @@ size_t trimul_epilogue_backward_workspace_bytes(const trimul_weights_t *w);
 trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, int64_t row_off,
                                          int64_t n_rows, int64_t col_off, int64_t n_cols,
                                          const float *x_acc, const void *z, const uint8_t *mask,
-                                         const float *dout, float *dx, float *dz,
+                                         const float *dout, float *dx, float *dz, uint32_t flags,
                                          const trimul_epilogue_grads_t *grads /* (host) */,
                                          void *workspace, size_t workspace_bytes, void *stream);
 

@@ -118,7 +118,7 @@ def lib():
         L.trimul_tile_backward.restype = ctypes.c_int
         L.trimul_epilogue_backward_workspace_bytes.argtypes = [W]
         L.trimul_epilogue_backward_workspace_bytes.restype = sz
-        L.trimul_epilogue_backward.argtypes = [W, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+        L.trimul_epilogue_backward.argtypes = [W, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, u32,
                                                ctypes.POINTER(_EpilogueGrads), vp, sz, vp]
         L.trimul_epilogue_backward.restype = ctypes.c_int
         L.trimul_tile_operands_backward_workspace_bytes.argtypes = [W]
@@ -383,7 +383,7 @@ def epilogue_backward_workspace_bytes(w: Weights) -> int:
 
 
 def epilogue_backward(w: Weights, n, row_off, n_rows, col_off, n_cols, x_acc, z, mask, dout, dx=None, dz=None,
-                      grads=None, workspace=None):
+                      grads=None, workspace=None, accumulate=False):
     """Backward of a tile's epilogue.
 
     ``x_acc`` is the tile's contraction result (accumulator layout, as
@@ -392,7 +392,7 @@ def epilogue_backward(w: Weights, n, row_off, n_rows, col_off, n_cols, x_acc, z,
     (dx, dz, grads): dx in the accumulator layout (may be passed as x_acc
     itself), dz [n_rows, n_cols, 128] (the output gate's share of dL/dz) and a
     dict of fp32 parameter gradients keyed as EPILOGUE_GRAD_SHAPES (allocated
-    when not given)."""
+    when not given; with ``accumulate`` the gradients are added to them)."""
     _need(x_acc, "x_acc", torch.float32, xacc_shape(n_rows, n_cols))
     _need(z, "z", w.torch_dtype, (n, n, C_Z))
     _need(mask, "mask", torch.uint8, (n, n))
@@ -414,7 +414,8 @@ def epilogue_backward(w: Weights, n, row_off, n_rows, col_off, n_cols, x_acc, z,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8)
     _check(lib().trimul_epilogue_backward(w.ref, n, row_off, n_rows, col_off, n_cols, _ptr(x_acc), _ptr(z),
-                                          _ptr(mask), _ptr(dout), _ptr(dx), _ptr(dz), ctypes.byref(g),
+                                          _ptr(mask), _ptr(dout), _ptr(dx), _ptr(dz),
+                                          GRAD_ACCUMULATE if accumulate else 0, ctypes.byref(g),
                                           _ptr(workspace), workspace.numel(), _stream()))
     return dx, dz, grads
 

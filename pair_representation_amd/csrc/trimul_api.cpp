@@ -527,7 +527,7 @@ size_t trimul_epilogue_backward_workspace_bytes(const trimul_weights_t *w) {
 trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, int64_t row_off, int64_t n_rows,
                                          int64_t col_off, int64_t n_cols, const float *x_acc, const void *z,
                                          const uint8_t *mask, const float *dout, float *dx, float *dz,
-                                         const trimul_epilogue_grads_t *grads, void *workspace,
+                                         uint32_t flags, const trimul_epilogue_grads_t *grads, void *workspace,
                                          size_t workspace_bytes, void *stream) {
   trimul_status_t st = check_weights(w);
   if (st != TRIMUL_OK) return st;
@@ -540,6 +540,7 @@ trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, i
     return fail(TRIMUL_ERR_INVALID_ARG, "x_acc, z, mask, dout, dx and dz are required");
   if (!aligned(x_acc, 16) || !aligned(z, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(dz, 16))
     return fail(TRIMUL_ERR_ALIGNMENT, "x_acc, z, dout, dx and dz must be 16-byte aligned");
+  if (flags & ~(uint32_t)TRIMUL_GRAD_ACCUMULATE) return fail(TRIMUL_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!grads) return fail(TRIMUL_ERR_INVALID_ARG, "grads is NULL");
   float *const gp[] = {grads->w_out_proj, grads->w_out_gate, grads->ln_out_w, grads->ln_out_b, grads->ln_in_w, grads->ln_in_b};
   const char *gn[] = {"w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b"};
@@ -583,6 +584,7 @@ trimul_status_t trimul_epilogue_backward(const trimul_weights_t *w, int64_t n, i
   a.g_ln_x_b = grads->ln_out_b;
   a.g_ln_z_w = grads->ln_in_w;
   a.g_ln_z_b = grads->ln_in_b;
+  a.grad_accumulate = a.ln_accumulate = (flags & TRIMUL_GRAD_ACCUMULATE) ? 1 : 0;
   const hipError_t e = trimul::launch_k3b(a, w->dtype, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "epilogue backward kernel launch");
   return ok();

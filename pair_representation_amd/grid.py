@@ -23,14 +23,18 @@ placing each tile of the result into the full output.
 An s x 1 split is the memory-bounded mode: the output is produced in row
 blocks, and the contraction result is held for one block at a time.
 
+emulate_backward runs the same grid's backward (the training step the pages
+make the point of the tiling): each tile's gradients from the library's three
+backward entry points, summed over the tiles.
+
 This module is host logic over the C ABI: it plans, allocates and calls; all
 arithmetic of the method runs in the library's kernels.
 """
 from dataclasses import dataclass, field
 from typing import List, Tuple
 
-from . import (INCOMING, OUTGOING, TILE_FIRST, TILE_LAST, Weights, new_operand, new_xacc, tile,
-               tile_operands)
+from . import (C_Z, EPILOGUE_GRAD_SHAPES, INCOMING, OUTGOING, PROJECTION_GRAD_SHAPES, TILE_FIRST, TILE_LAST, Weights,
+               epilogue_backward, new_operand, new_xacc, tile, tile_backward, tile_operands, tile_operands_backward)
 
 
 def split(n: int, parts: int) -> List[Tuple[int, int]]:
@@ -108,6 +112,63 @@ def emulate(z, mask, w: Weights, direction: int, s_rows: int, s_cols: int = None
                             z, mask)
         out[t.row_off:t.row_off + t.n_rows, t.col_off:t.col_off + t.n_cols].copy_(out_tile)
     return out
+
+
+def emulate_backward(z, mask, w: Weights, direction: int, dout, s_rows: int, s_cols: int = None):
+    """The grid's backward, every device step on this GPU: the gradients of
+    L = sum(dout * layer(z)) with respect to z and all ten parameters.
+
+    Each tile recomputes its forward state as a device would (its operand
+    blocks in ring order, the contraction result), then runs
+      - the epilogue's backward on its own pairs (its share of the gate path's
+        dL/dz and of the epilogue's parameter gradients),
+      - the contraction's backward over its blocks (dL/da, dL/db per block),
+      - the projections' backward of each block, which adds dL/dz at the
+        blocks' source pairs (owned by other devices of its ring: on a real
+        grid these partial sums travel back around the ring).
+    Parameter gradients are summed over all tiles by the library
+    (GRAD_ACCUMULATE).  Two passes: every tile's gate-path dL/dz is placed
+    before any projection backward adds to those pairs.  Returns
+    (dz [n, n, 128] fp32, grads dict keyed by parameter name)."""
+    import torch
+
+    n = z.shape[0]
+    dev = z.device
+    f32 = torch.float32
+    dz = torch.zeros((n, n, C_Z), dtype=f32, device=dev)
+    g_epi = {k: torch.zeros(shp, dtype=f32, device=dev) for k, shp in EPILOGUE_GRAD_SHAPES.items()}
+    g_proj = {k: torch.zeros(shp, dtype=f32, device=dev) for k, shp in PROJECTION_GRAD_SHAPES.items()
+              if not k.startswith("ln_in")}
+    g_proj["ln_in_w"], g_proj["ln_in_b"] = g_epi["ln_in_w"], g_epi["ln_in_b"]
+    tiles = plan(n, direction, s_rows, s_cols)
+
+    def forward_state(t):
+        ld = (max(kl for _, kl in t.k_blocks) + 63) // 64 * 64
+        blocks = []
+        for k_off, k_len in t.k_blocks:
+            a, b = tile_operands(w, direction, z, mask, t.row_off, t.n_rows, t.col_off, t.n_cols, k_off, k_len, ld)
+            blocks.append((k_off, k_len, a, b))
+        x = new_xacc(t.n_rows, t.n_cols, dev)
+        tile(w, n, t.row_off, t.n_rows, t.col_off, t.n_cols, blocks, TILE_FIRST, x)
+        return blocks, x
+
+    dxs = []
+    for t in tiles:                       # pass 1: epilogue backward per tile
+        _, x = forward_state(t)
+        dout_t = dout[t.row_off:t.row_off + t.n_rows, t.col_off:t.col_off + t.n_cols].contiguous()
+        dx, dz_t, _ = epilogue_backward(w, n, t.row_off, t.n_rows, t.col_off, t.n_cols, x, z, mask, dout_t,
+                                        grads=g_epi, accumulate=True)
+        dz[t.row_off:t.row_off + t.n_rows, t.col_off:t.col_off + t.n_cols].copy_(dz_t)   # placement
+        dxs.append(dx)
+    for t, dx in zip(tiles, dxs):         # pass 2: contraction and projections
+        blocks, _ = forward_state(t)
+        da, db = tile_backward(w, t.n_rows, t.n_cols, blocks, dx)
+        for (k_off, k_len, _, _), dai, dbi in zip(blocks, da, db):
+            tile_operands_backward(w, direction, z, mask, t.row_off, t.n_rows, t.col_off, t.n_cols, k_off, k_len,
+                                   da=dai, db=dbi, dz=dz, grads=g_proj, accumulate=True)
+    grads = dict(g_epi)
+    grads.update(g_proj)
+    return dz, grads
 
 
 def step_model(n: int, s: int, tflops: float, link_gbs: float, c: int = 128, elt_bytes: int = 2) -> dict:

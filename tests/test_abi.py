@@ -247,7 +247,7 @@ def test_backward_validation():
 
 def call_ebwd(w=None, n=100, row_off=10, n_rows=50, col_off=20, n_cols=40, x=FAKE, z=FAKE + 0x1000000,
               mask=FAKE + 0x2000000, dout=FAKE + 0x3000000, dx=FAKE + 0x4000000, dz=FAKE + 0x5000000,
-              grads="ok", null_grad=None, misalign_grad=None, ws=FAKE + 0x8000000, ws_bytes=None):
+              grads="ok", null_grad=None, misalign_grad=None, ws=FAKE + 0x8000000, ws_bytes=None, flags=0):
     L = pra.lib()
     w = weights() if w is None else w
     g = pra._EpilogueGrads(*[FAKE + 0x6000000 + 0x10000 * i for i in range(6)])
@@ -259,7 +259,7 @@ def call_ebwd(w=None, n=100, row_off=10, n_rows=50, col_off=20, n_cols=40, x=FAK
     if ws_bytes is None:
         ws_bytes = L.trimul_epilogue_backward_workspace_bytes(ctypes.byref(w))
     return L.trimul_epilogue_backward(ctypes.byref(w), n, row_off, n_rows, col_off, n_cols, x, z, mask, dout, dx,
-                                      dz, gp, ws, ws_bytes, None)
+                                      dz, flags, gp, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("dtype,elt", [(pra.BF16, 2), (pra.F32, 4)])
@@ -285,6 +285,7 @@ def test_epilogue_backward_validation():
     for name in ("x", "z", "dout", "dx", "dz"):
         assert call_ebwd(**{name: FAKE + 0x9000000 + 8}) == pra.ERR_ALIGNMENT, name
     assert call_ebwd(grads=None) == pra.ERR_INVALID_ARG
+    assert call_ebwd(flags=2) == pra.ERR_INVALID_ARG
     for name in ("w_out_proj", "w_out_gate", "ln_out_w", "ln_out_b", "ln_in_w", "ln_in_b"):
         assert call_ebwd(null_grad=name) == pra.ERR_INVALID_ARG, name
         assert call_ebwd(misalign_grad=name) == pra.ERR_ALIGNMENT, name

@@ -64,3 +64,28 @@ def test_grid_emulation_vs_oracle(case, direction):
     e = rel_err(emu.double().cpu().numpy(), ref)
     print(f"  vs Q-oracle {e:.3e}", flush=True)
     assert e <= 1e-2
+
+
+@pytest.mark.parametrize("direction", list(DIRS))
+@pytest.mark.parametrize("s_rows,s_cols", [(2, 2), (3, 2)])
+def test_grid_backward_matches_oracle(dev, direction, s_rows, s_cols):
+    """The grid's backward (grid.emulate_backward: each tile's share from the
+    three backward entry points, summed over tiles) in fp32 mode against
+    oracle.trimul_vjp: dL/dz and all ten parameter gradients, bar 1e-4 (the
+    forward's fp32 bar; the k-blocks only change the fp32 summation order)."""
+    import numpy as np
+    n = 71
+    print(f"[case] grid backward {s_rows}x{s_cols} {direction} n={n}", flush=True)
+    z, mask, wts = wl.make_small(n, seed=31, dtype="f32", device="cpu", random_ln=True, mask_keep=0.85)
+    w = pra.Weights(wts, pra.F32, device=dev)
+    dout = np.random.default_rng(32).standard_normal((n, n, pra.C_Z))
+    dz, grads = grid.emulate_backward(z.to(dev), mask.to(dev), w, DIRS[direction],
+                                      torch.from_numpy(dout).float().to(dev), s_rows, s_cols)
+    torch.cuda.synchronize()
+    ref = oracle.trimul_vjp(z.double().numpy(), mask.numpy(), wl.weights_f64(wts), direction, dout)
+    errs = {"z": rel_err(dz.double().cpu().numpy(), ref["z"])}
+    for k in oracle.WEIGHT_KEYS:
+        errs[k] = rel_err(grads[k].double().cpu().numpy(), ref[k])
+    print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= 1e-4, (k, v)
