@@ -1,18 +1,25 @@
-// K3B: backward of the epilogue (K3) for a tile of the pair grid.
+// K3B: backward of a gated, masked pair of 128 x 128 linear maps after
+// LayerNorm, on a grid of positions of the pair grid.  Epilogue mode: the
+// backward of K3 for a tile (x = the contraction result, W_y = W_out_proj,
+// W_t = W_out_gate, LN_x = the output and LN_z = the input LayerNorm).
+// Projection mode: the backward of one side of K1 (x = z, LN_x = LN_z = the
+// input LayerNorm, W_y / W_t = the side's projection / gate matrix, positions
+// = the operand entries of a chunk, mapped to their source pairs).
 //
-// Forward, per pair: n = LN_out(x) = x^ g_o + b_o, y = W_o n,
-// zh = LN_in(z) = z^ g_i + b_i, t = W_g zh, s = sigmoid(t), out = m s y.
+// Forward, per pair: n = LN_x(x) = x^ g_x + b_x, y = W_y n,
+// zh = LN_z(z) = z^ g_z + b_z, t = W_t zh, s = sigmoid(t), out = m s y.
 // Given dout = dL/dout the kernel writes, per pair,
 //   dy = m s dout,  dt = m y dout s (1 - s)
-//   dn = W_o^T dy,  dx = LN backward of dn * g_o   (the input of the
-//                                                  contraction's backward)
-//   dzh = W_g^T dt, dz = LN backward of dzh * g_i  (the gate path's share of
-//                                                  dL/dz)
-// and, for the parameters, the sums over the tile's pairs
+//   dn = W_y^T dy,  dx = LN backward of dn * g_x   (epilogue: the input of
+//                                                  the contraction's backward)
+//   dzh = W_t^T dt, dz = LN backward of dzh * g_z  (epilogue: the gate path's
+//                                                  share of dL/dz)
+// (projection mode: one LayerNorm backward of both, added to a global dL/dz)
+// and, for the parameters, the sums over the grid's pairs
 //   G = sum dy x^T,  S = sum dy,  H = sum dt z^T,  T = sum dt
-// from which dW_o = G diag(g_o) + S b_o^T, dg_o = colsum(W_o * G),
-// db_o = W_o^T S (the gate's parameters likewise from H, T): the weight
-// gradients become two 128 x 128 accumulators per work-group instead of six.
+// from which dW_y = G diag(g_x) + S b_x^T, dg_x = colsum(W_y * G),
+// db_x = W_y^T S (W_t and LN_z likewise from H, T): the weight gradients
+// become two 128 x 128 accumulators per work-group instead of six.
 //
 // Work item: 32 pairs = 4 rows x 8 columns as in K3 (pair p = 4*jj + ii, the
 // order of one channel's values in the x layout).  One work-group of 4 waves
@@ -231,8 +238,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int E = sizeof(T);
   constexpr bool kWeightsInRegs = (E == 2);
   using Op = OpB<T>;
-  __shared__ __attribute__((aligned(16))) unsigned char n_ops[Op::BYTES];    // LN_out(x)
-  __shared__ __attribute__((aligned(16))) unsigned char z_ops[Op::BYTES];    // -log2(e) LN_in(z)
+  __shared__ __attribute__((aligned(16))) unsigned char n_ops[Op::BYTES];    // LN_x(x)
+  __shared__ __attribute__((aligned(16))) unsigned char z_ops[Op::BYTES];    // -log2(e) LN_z(z)
   __shared__ __attribute__((aligned(16))) unsigned char dy_ops[Op::BYTES];   // dy
   __shared__ __attribute__((aligned(16))) unsigned char dt_ops[Op::BYTES];   // dt
   __shared__ __attribute__((aligned(16))) float xh_pl[kC * kPairs];          // x^ [channel][pair]
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(16))) float dt_pl[kC * kPairs];          // dt
   __shared__ __attribute__((aligned(16))) float4 part_f[kGroups][kPairs];    // per-group moments of x and z
   __shared__ __attribute__((aligned(16))) float4 part_b[4][kPairs];          // per-wave LN-backward sums
-  __shared__ __attribute__((aligned(16))) float ln[4][kC];                   // g_o, b_o, g_i, b_i
+  __shared__ __attribute__((aligned(16))) float ln[4][kC];                   // g_x, b_x, g_z, b_z
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __syncthreads();   // (2)
 
     // ---- accumulator layout: recompute y and the gate --------------------
-    f32x16 a0, a1;   // y = W_o n and -log2(e) t, then dn and dzh
+    f32x16 a0, a1;   // y = W_y n and -log2(e) t, then dn and dzh
 #pragma unroll
     for (int e = 0; e < 16; ++e) { a0[e] = 0.f; a1[e] = 0.f; }
     {
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
 
-    // ---- dn = W_o^T dy, dzh = W_g^T dt (rows 32w .. +31, all 32 pairs) ------
+    // ---- dn = W_y^T dy, dzh = W_t^T dt (rows 32w .. +31, all 32 pairs) ------
 #pragma unroll
     for (int e = 0; e < 16; ++e) { a0[e] = 0.f; a1[e] = 0.f; }
     {
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     // ---- LayerNorm backward: per-pair sums over the 128 channels of
-    //      g = dn * g_o and h = dzh * g_i; g and h are kept in this wave's
+    //      g = dn * g_x and h = dzh * g_z; g and h are kept in this wave's
     //      own rows of the dy / dt planes (read back after the barrier) -------
     {
       float sg = 0.f, sgx = 0.f, sh = 0.f, shz = 0.f;
