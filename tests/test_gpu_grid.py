@@ -67,10 +67,11 @@ def test_grid_emulation_vs_oracle(case, direction):
 
 
 @pytest.mark.parametrize("direction", list(DIRS))
-@pytest.mark.parametrize("s_rows,s_cols", [(2, 2), (3, 2)])
+@pytest.mark.parametrize("s_rows,s_cols", [(2, 2), (3, 2), (3, 1)])
 def test_grid_backward_matches_oracle(dev, direction, s_rows, s_cols):
     """The grid's backward (grid.emulate_backward: each tile's share from the
-    three backward entry points, summed over tiles) in fp32 mode against
+    three backward entry points, summed over tiles; 3 x 1 is the memory-bounded
+    row-block mode) in fp32 mode against
     oracle.trimul_vjp: dL/dz and all ten parameter gradients, bar 1e-4 (the
     forward's fp32 bar; the k-blocks only change the fp32 summation order)."""
     import numpy as np
