@@ -227,7 +227,8 @@ trimul_status_t trimul_tile_backward(const trimul_weights_t *w, int64_t n_rows, 
                                      float *const *db_out /* (host) */, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
-/* Parameter gradients of the epilogue, fp32, each fully overwritten. */
+/* Parameter gradients of the epilogue, fp32: overwritten, or added to with
+ * TRIMUL_GRAD_ACCUMULATE. */
 typedef struct {
   float *w_out_proj;           /* [c_z][c]   dL/dW_out_proj                      */
   float *w_out_gate;           /* [c_z][c_z] dL/dW_out_gate                      */
