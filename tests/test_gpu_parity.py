@@ -177,14 +177,14 @@ def test_operand_planes(dev, dtype, direction):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("m_rows,n_cols,klen", [(1, 1, 1), (40, 300, 77), (256, 256, 256), (300, 129, 515),
                                                  (277, 300, 70), (21, 533, 64), (513, 31, 33), (150, 150, 70),
-                                                 (356, 533, 64), (100, 700, 40)])
+                                                 (356, 533, 64), (100, 700, 40), (21, 533, 515), (280, 533, 200)])
 def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     """Contraction kernel fed the oracle's operands directly (uploaded, exact in
     the storage dtype) vs their float64 contraction.  The shapes include edge
     tiles with a few valid rows or columns past a 256 boundary (277 = 256 + 21,
     533 = 512 + 21, 513), single short tiles (21, 31), and edge tiles whose
     valid 32-blocks are spread unevenly over the waves (150, 356 = 256 + 100,
-    700 = 384 + 316)."""
+    700 = 384 + 316), with 1 to 9 k-tiles."""
     r = np.random.default_rng(m_rows * 7 + n_cols)
     ld = (klen + 63) // 64 * 64
     a = r.standard_normal((128, m_rows, klen))
@@ -207,6 +207,37 @@ def test_contraction_kernel_alone(dev, dtype, m_rows, n_cols, klen):
     ref = np.matmul(a, b.transpose(0, 2, 1))
     e = rel_err(pra.xacc_to_planar(x, m_rows, n_cols).cpu().double().numpy(), ref)
     print(f"  contraction {dtype} {m_rows}x{n_cols}x{klen}: {e:.3e}")
+    assert e <= 1e-5
+
+
+@pytest.mark.parametrize("m_rows,n_cols,k_lens", [(277, 533, (70, 64, 130, 1, 200)), (21, 300, (129, 3, 64))])
+def test_contraction_edge_tiles_over_chunks(dev, m_rows, n_cols, k_lens):
+    """bf16 edge tiles (rows 256..276 by 384 columns, columns 384..532, the
+    21 x 300 tile) walking k-tiles across chunk boundaries with ragged chunk
+    lengths, vs the float64 contraction of the concatenated operands."""
+    print(f"[case] contraction edge tiles {m_rows}x{n_cols} chunks {k_lens}", flush=True)
+    r = np.random.default_rng(m_rows + 3 * n_cols)
+    a_parts, b_parts, chunks, k0 = [], [], [], 0
+    for kl in k_lens:
+        ld = (kl + 63) // 64 * 64
+        a = oracle.bf16_round(r.standard_normal((128, m_rows, kl)))
+        b = oracle.bf16_round(r.standard_normal((128, n_cols, kl)))
+        A = torch.zeros((128, m_rows, ld), dtype=torch.bfloat16)
+        B = torch.zeros((128, n_cols, ld), dtype=torch.bfloat16)
+        A[:, :, :kl] = torch.from_numpy(a).to(torch.bfloat16)
+        B[:, :, :kl] = torch.from_numpy(b).to(torch.bfloat16)
+        chunks.append((k0, kl, pra.planar_to_operand(A.to(dev)), pra.planar_to_operand(B.to(dev))))
+        a_parts.append(a)
+        b_parts.append(b)
+        k0 += kl
+    _, _, wts = wl.make_small(4, seed=1, dtype="bf16", device="cpu")
+    w = pra.Weights(wts, pra.BF16, device=dev)
+    x = pra.new_xacc(m_rows, n_cols, dev).fill_(float("nan"))
+    pra.tile(w, max(m_rows, n_cols, k0), 0, m_rows, 0, n_cols, chunks, pra.TILE_FIRST, x)
+    torch.cuda.synchronize()
+    ref = np.matmul(np.concatenate(a_parts, axis=2), np.concatenate(b_parts, axis=2).transpose(0, 2, 1))
+    e = rel_err(pra.xacc_to_planar(x, m_rows, n_cols).cpu().double().numpy(), ref)
+    print(f"  contraction edge tiles {m_rows}x{n_cols} chunks {k_lens}: {e:.3e}", flush=True)
     assert e <= 1e-5
 
 
