@@ -687,6 +687,11 @@ def main():
         "per_direction": per_dir,
         "cpu_baseline": None,
     }
+    n_valid = int(wl.residue_mask(work).sum())
+    if n_valid < n:
+        # the same time counted over the pairs of unmasked residues only
+        # (padding and masked residues still cost their share of the work)
+        rec["valid_view"] = {"n_valid": n_valid, "valid_pair_updates_per_s": value * (n_valid / n) ** 2}
     del ws, out_o, out_i, z, mask
     torch.cuda.empty_cache()
     if args.cpu_rows > 0:
