@@ -64,6 +64,35 @@ def traffic_from_profile(kernel_src):
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
 
 
+def blas_threads():
+    """Threads of the BLAS library numpy's products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def host_cpu(blas_threads):
+    """The host the oracle ran on: CPU model, logical CPUs visible to this
+    process, and the BLAS thread count the oracle's products used."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable,
+            "blas_threads": int(blas_threads)}
+
+
 def cpu_baseline(work, block_rows):
     """Oracle phase rates on blocks of the workload, extrapolated to the job.
 
@@ -76,11 +105,7 @@ def cpu_baseline(work, block_rows):
     import numpy as np
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     n = work.n
     rb = block_rows
     w = wl.weights_f64(wl.make_weights(work.c_z, work.c, work.seed, work.dtype))
@@ -104,6 +129,7 @@ def cpu_baseline(work, block_rows):
         "unit": "pair-updates/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": host_cpu(threads),
         "sample": (f"float64 oracle phases on blocks of {work.name}: projection of {rb}x{n} pairs "
                    f"{t1 - t0:.2f}s, contraction {rb}x{4 * rb}x{n}x128 {t2 - t1:.2f}s, epilogue {rb}x{rb} "
                    f"pairs {t3 - t2:.2f}s; extrapolated (projection, epilogue x N^2; contraction x N^3) "
@@ -254,6 +280,7 @@ def cpu_baseline_backward(work, block_rows, block_k=128):
     scale = (n / block_rows) * (n / block_k) * 2.0
     t_full = t_blk * scale
     return {"value": n * n / t_full, "unit": "pair-gradients/s", "cores": os.cpu_count(), "kind": "oracle",
+            "host": host_cpu(blas_threads()),
             "sample": f"oracle.contract_rows_vjp: {block_rows} rows of dX against {block_k} k-columns of a "
                       f"{n}-row b ({t_blk:.2f}s), extrapolated x{scale:.0f} to both gradients of the "
                       f"{n}x{n} grid ({t_full:.0f}s)"}
@@ -482,6 +509,7 @@ def cpu_baseline_atom_attention(cfg, n_sample=28840):
     rate = n_sample / dt
     total = cfg["batch"] * cfg["n_atoms"]
     return {"value": rate, "unit": "query-atoms/s", "cores": os.cpu_count(), "kind": "oracle",
+            "host": host_cpu(blas_threads()),
             "sample": f"oracle window_attention on one sequence of {n_sample} atoms ({dt:.2f}s); the "
                       f"{total} query atoms of the workload would take {total / rate:.0f}s"}
 
@@ -507,6 +535,7 @@ def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
     rate = block * blocks / t_sum
     n = work.n
     return {"value": rate, "unit": "pairs/s", "cores": os.cpu_count(), "kind": "oracle",
+            "host": host_cpu(blas_threads()),
             "sample": f"oracle.finish_vjp on {blocks} blocks of {block} seeded pairs ({t_sum:.2f}s); the "
                       f"{n}x{n} grid would take {n * n / rate:.0f}s"}
 
