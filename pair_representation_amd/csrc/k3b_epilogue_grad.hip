@@ -378,7 +378,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int c = 0; c < kPer; ++c) xv[c] = zf[c];
     }
     {
-      const float2 mx = moments16(xv), mz = moments16(zf);
+      // (projection mode: x is z and both LayerNorms are ln_in, so every
+      // quantity of the z side below equals the x side's and is not redone)
+      const float2 mx = moments16(xv), mz = kProj ? mx : moments16(zf);
       part_f[grp][q] = make_float4(mx.x, mx.y, mz.x, mz.y);
     }
     __syncthreads();   // (1)
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         px[g] = make_float2(v.x, v.y);
         pz[g] = make_float2(v.z, v.w);
       }
-      const float2 sx = merge8(px, p.eps), sz = merge8(pz, p.eps);
+      const float2 sx = merge8(px, p.eps), sz = kProj ? sx : merge8(pz, p.eps);
       rx = sx.y;
       rz = sz.y;
       // normalised values; zero for pairs that are not kept, whose x may be
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
         xv[c] = keep ? (xv[c] - sx.x) * rx : 0.f;
-        zf[c] = keep ? (zf[c] - sz.x) * rz : 0.f;
+        zf[c] = kProj ? xv[c] : (keep ? (zf[c] - sz.x) * rz : 0.f);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int i = 0; i < 8; ++i) {
           const int c = c0 + 8 * u + i;
           fn[i] = xv[8 * u + i] * ln[0][c] + ln[1][c];
-          fz[i] = (zf[8 * u + i] * ln[2][c] + ln[3][c]) * kNegLog2e;
+          fz[i] = kProj ? fn[i] * kNegLog2e : (zf[8 * u + i] * ln[2][c] + ln[3][c]) * kNegLog2e;
         }
         Op::put8(n_ops, q, c0 / 8 + u, fn);
         Op::put8(z_ops, q, c0 / 8 + u, fz);
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
         xh_pl[pl(c0 + c, q)] = xv[c];
-        zh_pl[pl(c0 + c, q)] = zf[c];
+        if constexpr (!kProj) zh_pl[pl(c0 + c, q)] = zf[c];   // projection mode reads x^ for z^
       }
     }
     __syncthreads();   // (2)
@@ -478,7 +480,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int kb = 0; kb < 4; ++kb) {
         PFrag<T> bx, bz;
         bx.load(xh_pl, 32 * kb + (lane & 31), p0);
-        bz.load(zh_pl, 32 * kb + (lane & 31), p0);
+        if constexpr (kProj) bz = bx;
+        else bz.load(zh_pl, 32 * kb + (lane & 31), p0);
         mma_pp(G[kb], ay, bx);
         mma_pp(H[kb], at, bz);
       }
@@ -520,12 +523,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           const int e = 4 * g4 + i;
           const int k = o0 + acc_row(e, lane);
           const float g = a0[e] * vo[i], h = a1[e] * vi[i];
-          sg += g;
-          sgx += g * xh_pl[pl(k, q)];
-          sh += h;
-          shz += h * zh_pl[pl(k, q)];
-          dy_pl[pl(k, q)] = g;
-          dt_pl[pl(k, q)] = h;
+          if constexpr (kProj) {
+            // one LayerNorm: only g + h and its sums are needed
+            const float gh = g + h;
+            sg += gh;
+            sgx += gh * xh_pl[pl(k, q)];
+            dy_pl[pl(k, q)] = gh;
+          } else {
+            sg += g;
+            sgx += g * xh_pl[pl(k, q)];
+            sh += h;
+            shz += h * zh_pl[pl(k, q)];
+            dy_pl[pl(k, q)] = g;
+            dt_pl[pl(k, q)] = h;
+          }
         }
       }
       sg += __shfl_xor(sg, 32, 64);
@@ -547,7 +558,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const int64_t r = blk * 4 + (q & 3), col = s0 + (q >> 2);
       if constexpr (kProj) {
         // one LayerNorm (x = z): dz = r (g + h - mean(g + h) - z^ mean((g + h) z^)),
-        // added to the pair's row of the global dz
+        // added to the pair's row of the global dz (g + h and its sums sit in
+        // the dy plane and in mg, mgx; mh = mhz = 0)
         float *const dzrow = p.dz + pair_of(r, col) * kCz + o0 + 4 * hl;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -555,7 +567,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int k = o0 + acc_row(4 * g4 + i, lane);
-            const float v = rz * (dy_pl[pl(k, q)] + dt_pl[pl(k, q)] - (mg + mh) - zh_pl[pl(k, q)] * (mgx + mhz));
+            const float v = rz * (dy_pl[pl(k, q)] - mg - xh_pl[pl(k, q)] * mgx);
             vz[i] += keep ? v : 0.f;
           }
           *reinterpret_cast<f32x4 *>(dzrow + 8 * g4) = vz;
