@@ -14,7 +14,8 @@
 //                                                  the contraction's backward)
 //   dzh = W_t^T dt, dz = LN backward of dzh * g_z  (epilogue: the gate path's
 //                                                  share of dL/dz)
-// (projection mode: one LayerNorm backward of both, added to a global dL/dz)
+// (projection mode: x^ = z^, so the normalised input is formed once, and one
+// LayerNorm backward of dn * g + dzh * g is added to a global dL/dz)
 // and, for the parameters, the sums over the grid's pairs
 //   G = sum dy x^T,  S = sum dy,  H = sum dt z^T,  T = sum dt
 // from which dW_y = G diag(g_x) + S b_x^T, dg_x = colsum(W_y * G),
