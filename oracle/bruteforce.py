@@ -44,25 +44,68 @@ def _matvec(W, v):
     return out
 
 
-def trimul_loops(z, mask, w, direction, eps=1e-5):
+def bf16_nearest(t):
+    """The bfloat16 value nearest to the float t, ties to the even neighbour.
+
+    bfloat16 has 8 significant bits and float32's exponent range.  For a
+    normal t = m * 2**e (0.5 <= |m| < 1) the spacing of bfloat16 values around
+    t is 2**(e - 8); below 2**-126 it is the fixed 2**-133.  t divided by the
+    spacing is a float with at most 9 integer bits, so Python's round() (which
+    rounds halves to the even integer) picks the neighbour exactly.  Values
+    that round to 2**128 or beyond become infinite."""
+    if t == 0.0 or math.isinf(t) or math.isnan(t):
+        return t
+    if abs(t) >= 2.0 ** -126:
+        _, e = math.frexp(t)
+        q = e - 8
+    else:
+        q = -133
+    r = round(math.ldexp(t, -q))
+    if abs(r) >= 2 ** (128 - q):
+        return math.copysign(math.inf, t)
+    return math.ldexp(float(r), q)
+
+
+def project_loops(z, mask, w, quant=False, eps=1e-5):
+    """The gated a/b operands of every pair, as nested lists [N][N][c].
+
+    quant=True adds the two roundings to bfloat16 of a bf16 matrix-core
+    contraction: the normalised input after its affine map (gamma, beta),
+    where it enters the four projections, and the finished a and b values.
+    """
+    n = len(z)
+    W = {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()}
+    c = len(W["w_a_proj"])
+    a = [[None] * n for _ in range(n)]
+    b = [[None] * n for _ in range(n)]
+    for i in range(n):
+        for j in range(n):
+            zh = _ln(list(map(float, z[i][j])), W["ln_in_w"], W["ln_in_b"], eps)
+            if quant:
+                zh = [bf16_nearest(t) for t in zh]
+            m = 1.0 if mask[i][j] else 0.0
+            ap = _matvec(W["w_a_proj"], zh)
+            ag = _matvec(W["w_a_gate"], zh)
+            bp = _matvec(W["w_b_proj"], zh)
+            bg = _matvec(W["w_b_gate"], zh)
+            a[i][j] = [m * _sig(ag[d]) * ap[d] for d in range(c)]
+            b[i][j] = [m * _sig(bg[d]) * bp[d] for d in range(c)]
+            if quant:
+                a[i][j] = [bf16_nearest(t) for t in a[i][j]]
+                b[i][j] = [bf16_nearest(t) for t in b[i][j]]
+    return a, b
+
+
+def trimul_loops(z, mask, w, direction, eps=1e-5, quant=False):
     """z: nested lists [N][N][c_z]; mask: [N][N]; w: dict of nested lists.
-    Returns out as nested lists [N][N][c_z]."""
+    Returns out as nested lists [N][N][c_z].  quant=True rounds the
+    contraction operands as ``project_loops`` does; nothing else is rounded."""
     n = len(z)
     W = {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()}
     c = len(W["w_a_proj"])
     zh = [[_ln(list(map(float, z[i][j])), W["ln_in_w"], W["ln_in_b"], eps) for j in range(n)]
           for i in range(n)]
-    a = [[None] * n for _ in range(n)]
-    b = [[None] * n for _ in range(n)]
-    for i in range(n):
-        for j in range(n):
-            m = 1.0 if mask[i][j] else 0.0
-            ap = _matvec(W["w_a_proj"], zh[i][j])
-            ag = _matvec(W["w_a_gate"], zh[i][j])
-            bp = _matvec(W["w_b_proj"], zh[i][j])
-            bg = _matvec(W["w_b_gate"], zh[i][j])
-            a[i][j] = [m * _sig(ag[d]) * ap[d] for d in range(c)]
-            b[i][j] = [m * _sig(bg[d]) * bp[d] for d in range(c)]
+    a, b = project_loops(z, mask, w, quant, eps)
     out = [[None] * n for _ in range(n)]
     for i in range(n):
         for j in range(n):

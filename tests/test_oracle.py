@@ -380,6 +380,98 @@ def test_qmode_is_close_to_but_not_exact():
     assert 1e-4 < e < 6e-2
 
 
+def test_bf16_nearest_agrees_with_oracle_rounding():
+    """The scalar-loop rounding (math.frexp + round) and the oracle's
+    vectorised one (frexp + rint) agree on normal values, exact ties, values
+    one float64 step either side of a tie, subnormals and overflow."""
+    r = np.random.default_rng(140)
+    vals = list(r.standard_normal(2000) * np.exp2(r.integers(-40, 40, 2000)))
+    for k in range(1, 300):                      # ties between neighbours 1 + (k-1)/128 and 1 + k/128
+        t = 1.0 + (2 * k - 1) / 256.0
+        vals += [t, -t, np.nextafter(t, 0.0), np.nextafter(t, 9.0), t * 2.0 ** -130]
+    vals += [0.0, -0.0, 2.0 ** -140, 3 * 2.0 ** -134, 1e-45, (2 - 2 ** -8) * 2.0 ** 127, 3.4e38, 1e39]
+    got = np.array([bruteforce.bf16_nearest(float(v)) for v in vals])
+    assert np.array_equal(got, oracle.bf16_round(np.array(vals)))
+
+
+@pytest.mark.parametrize("n,c_z,c", [(3, 8, 4), (2, 128, 128)])
+def test_qmode_project_matches_loops(n, c_z, c):
+    """Q-mode operands equal the scalar-loop spelling's exactly: zh rounded
+    after its affine map, a and b rounded when finished."""
+    w = rand_weights(c_z, c, 141 + n)
+    z, m = rand_inputs(n, c_z, 142 + n, keep=0.8)
+    a, b = oracle.project(z, m, w, quant=True)
+    la, lb = bruteforce.project_loops(z.tolist(), m.tolist(), w, quant=True)
+    assert np.array_equal(a, np.array(la)) and np.array_equal(b, np.array(lb))
+    # and the rounding matters at these sizes: the exact operands differ
+    ea, _ = oracle.project(z, m, w)
+    assert np.max(np.abs(ea - a)) > 0
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_qmode_trimul_matches_loops(direction):
+    n, c_z, c = 4, 8, 8
+    w = rand_weights(c_z, c, 150)
+    z, m = rand_inputs(n, c_z, 151, keep=0.8)
+    got = oracle.trimul(z, m, w, direction, quant=True)
+    want = np.array(bruteforce.trimul_loops(z.tolist(), m.tolist(), w, direction, quant=True))
+    assert rel(got, want) < 1e-12
+
+
+def test_qmode_rounding_point_worked_by_hand():
+    """One pair, c_z = 4, c = 2, worked by hand.  z = (-3, -1, 1, 3) has mean 0
+    and biased variance 5, so LN gives zhh = z / sqrt(5 + 1e-5), i.e.
+    zhh_0 = -1.3416394..., zhh_3 = 1.3416394...  The gates are zero
+    (sigmoid = 1/2) and W_ap picks 3 * channel 0 (row 0) and 3 * channel 3
+    (row 1), so a_d = 1.5 * zh.
+
+    Channel 0, gamma 1.3, beta 0.5: zh_0 = 1.3 * zhh_0 + 0.5 = -1.2441313.
+    bf16 spacing on [1, 2) is 2^-7: -1.2441313 * 128 = -159.25 -> -159, so
+    bf16(zh_0) = -1.2421875 and a_0 = 1.5 * -1.2421875 = -1.86328125 =
+    -238.5 * 2^-7, an exact tie -> even -238 -> a_0 = -1.859375.
+    Dropping the zh rounding gives 1.5 * -1.2441313 = -1.8661969 -> -238.87 ->
+    a_0 = -1.8671875; rounding before the affine map gives
+    1.5 * (1.3 * bf16(-1.3416394) + 0.5) = 1.5 * (1.3 * -1.34375 + 0.5) =
+    -1.8703125 -> -239.4 -> -1.8671875.
+
+    Channel 3, gamma 1.25, beta 0.5: zh_3 = 2.1770493; spacing on [2, 4) is
+    2^-6: 139.33 -> 139 -> 2.171875; a_1 = 1.5 * 2.171875 = 3.2578125 =
+    208.5 * 2^-6, a tie -> even 208 -> 3.25.  Without the zh rounding:
+    3.2655740 -> 208.997 -> 3.265625; rounding before the affine map:
+    1.5 * (1.25 * 1.34375 + 0.5) = 3.26953125 -> 209.25 -> 3.265625.
+    """
+    c_z, c = 4, 2
+    w = {
+        "w_a_proj": np.array([[3.0, 0, 0, 0], [0, 0, 0, 3.0]]), "w_a_gate": np.zeros((c, c_z)),
+        "w_b_proj": np.zeros((c, c_z)), "w_b_gate": np.zeros((c, c_z)),
+        "w_out_gate": np.zeros((c_z, c_z)), "w_out_proj": np.zeros((c_z, c)),
+        "ln_in_w": np.array([1.3, 1.0, 1.0, 1.25]), "ln_in_b": np.array([0.5, 0.0, 0.0, 0.5]),
+        "ln_out_w": np.ones(c), "ln_out_b": np.zeros(c),
+    }
+    z = np.array([[[-3.0, -1.0, 1.0, 3.0]]])
+    m = np.ones((1, 1), np.uint8)
+    a, _ = oracle.project(z, m, w, quant=True)
+    assert a[0, 0, 0] == -1.859375 and a[0, 0, 1] == 3.25
+    la, _ = bruteforce.project_loops(z.tolist(), m.tolist(), w, quant=True)
+    assert la[0][0] == [-1.859375, 3.25]
+    # the unrounded operands, for contrast
+    a_exact, _ = oracle.project(z, m, w)
+    assert oracle.bf16_round(a_exact)[0, 0].tolist() == [-1.8671875, 3.265625]
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_qmode_sampled_and_blockwise_match_full(direction):
+    n, c_z, c = 20, 8, 4
+    w = rand_weights(c_z, c, 160)
+    z, m = rand_inputs(n, c_z, 161, keep=0.9)
+    out = oracle.trimul(z, m, w, direction, quant=True)
+    rows, cols = np.array([0, 4, 19, 11]), np.array([19, 0, 7])
+    gz, gm = array_getters(z, m)
+    s = oracle.trimul_sampled(gz, gm, n, w, direction, rows, cols, quant=True)
+    assert np.max(np.abs(s - out[np.ix_(rows, cols)])) < 1e-13
+    assert np.max(np.abs(oracle.trimul_blockwise(z, m, w, direction, quant=True, block=6) - out)) < 1e-13
+
+
 # ---------------------------------------------------------------------------
 # stored regression fixture (written by tests/golden/make_golden.py from the
 # brute-force loops only)
