@@ -200,6 +200,56 @@ def bench_tile(work, args, dev):
             "config": {"workload": work.name, "n": work.n, "tile": t}, "directions": res}
 
 
+def bench_chunked(work, args, dev):
+    """The memory-bounded forward (trimul_forward_chunked) on a grid whose
+    whole-grid workspace does not fit beside z and the output: both
+    directions, timed with HIP events on the launch stream around each call.
+    Reports pair updates per second, the device memory held (z, mask, out and
+    the workspace) against the whole-grid path's, and the contraction's
+    matrix-core rate over the whole call (a lower bound: the call also runs
+    the projections, rebuilt per row block, and the epilogue)."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    n = work.n
+    cb = work.chunked
+    log(f"[bench] generating {work.name} (N={n}) on the GPU")
+    z, mask, wts = wl.make_inputs(work, dev)
+    w = pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev)
+    blocks = (cb["row_block"], cb["col_block"], cb["k_block"])
+    ws = torch.empty(pra.chunked_workspace_bytes(w, n, *blocks), dtype=torch.uint8, device=dev)
+    out = torch.empty((n, n, C_Z), dtype=torch.float32, device=dev)
+    res = {}
+    for d, name in ((pra.OUTGOING, "outgoing"), (pra.INCOMING, "incoming")):
+        for _ in range(args.warmup):
+            pra.forward_chunked(z, mask, w, d, *blocks, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            pra.forward_chunked(z, mask, w, d, *blocks, workspace=ws, out=out)
+            e[1].record()
+            evs.append(e)
+        torch.cuda.synchronize()
+        t = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs) * 1e-3
+        res[name] = {"ms": t * 1e3, "pair_updates_per_s": n * n / t,
+                     "contraction_TFLOP/s_over_call": 2.0 * n ** 3 * C / t / 1e12}
+        log(f"[bench] {name}: {t * 1e3:.1f} ms")
+    io = z.numel() * z.element_size() + mask.numel() + out.numel() * 4
+    t_both = sum(r["ms"] for r in res.values()) * 1e-3
+    return {"metric": "TriMul pair-updates/s, memory-bounded form (both directions)", "value": 2 * n * n / t_both,
+            "unit": "pair-updates/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": t_both * 1e3, "higher_is_better": True, "dtype": work.dtype, "data": "synthetic",
+            "config": {"workload": work.name, "n": n, "blocks": dict(cb)},
+            "device_bytes": {"z_mask_out": io, "workspace": ws.numel(), "total": io + ws.numel(),
+                             "whole_grid_path_total": io + pra.workspace_bytes(w, n),
+                             "device_total": torch.cuda.get_device_properties(dev).total_memory},
+            "directions": res}
+
+
 def bench_backward(work, args, dev):
     """Backward of the contraction step (trimul_tile_backward) on the whole
     N x N grid as one tile and one chunk: dA = dX B and dB = dX^T A per
@@ -540,6 +590,106 @@ def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
                       f"{n}x{n} grid would take {n * n / rate:.0f}s"}
 
 
+STREAM_MIXES = (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("k1_mix_1r_2w", 1, 2), ("k3_mix_3r_2w", 3, 2))
+
+
+def bench_peaks(args, dev):
+    """Achievable peaks on this GPU (libtrimul_peaks.so): the bf16
+    matrix-core loop (no memory traffic; each wave also reads the shader
+    clock and the real-time counter, giving the clock it ran at) and streaming
+    kernels at the byte mixes of the projection (1 read : 2 written) and
+    epilogue (3 : 2) kernels, plus plain read, write and copy; each streaming
+    launch moves about 6 GiB (far beyond the 256 MB last-level cache) and is
+    run in four forms (plain or non-temporal accesses, 4 or 8 elements in
+    flight per thread) at several grid sizes, the best average reported.  Times are HIP
+    events on the launch stream."""
+    import ctypes
+
+    import torch
+
+    from pair_representation_amd import build as pbuild
+
+    if not os.path.exists(pbuild.PEAKS_LIB):
+        raise RuntimeError(f"{pbuild.PEAKS_LIB} is missing: build it with `python -m pair_representation_amd.build`")
+    L = ctypes.CDLL(pbuild.PEAKS_LIB)
+    vp = ctypes.c_void_p
+    L.peaks_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.peaks_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_longlong, vp,
+                               ctypes.c_int, vp]
+    L.peaks_wall_clock_khz.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    khz = L.peaks_wall_clock_khz()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e-3
+
+    out = {"cus": cus, "wall_clock_khz": khz}
+    # matrix-core loop: one 8-wave work-group per CU, sized to run ~40 ms
+    blocks, iters = cus, 120000
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    clk = torch.zeros(blocks * 8 * 2, dtype=torch.int64, device=dev)
+
+    def mfma():
+        st = L.peaks_mfma(blocks, iters, vp(sink.data_ptr()), vp(clk.data_ptr()), sp)
+        if st != 0:
+            raise RuntimeError(f"peaks_mfma: hip error {st}")
+
+    t = timed(mfma, 3)
+    flops = float(blocks) * 8 * iters * 8 * 32768
+    c = clk.view(-1, 2).double()
+    clock_ghz = float(c[:, 0].sum() / c[:, 1].sum()) * khz * 1e-6 if khz > 0 else None
+    out["mfma_bf16"] = {"TFLOP/s": flops / t / 1e12, "frac_of_2500": flops / t / 1e12 / PEAK_BF16_TFLOPS,
+                        "ms": t * 1e3, "shader_clock_GHz": clock_ghz,
+                        "kernel": "peak_mfma: 8 independent 32x32x16 bf16 chains per wave, 2 waves per SIMD"}
+    log(f"[peaks] mfma {out['mfma_bf16']['TFLOP/s']:.0f} TFLOP/s at {clock_ghz} GHz")
+    # streaming kernels
+    total = 6 << 30
+    u32sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    res = {}
+    for name, r, w in STREAM_MIXES:
+        units = total // (16 * (r + w))
+        src = torch.empty(max(r, 1) * units * 16, dtype=torch.uint8, device=dev) if r else None
+        if src is not None:
+            src.fill_(7)
+        dst = torch.empty(w * units * 16, dtype=torch.uint8, device=dev) if w else None
+        best = None
+        for variant in range(4):
+            for per_cu in (4, 8, 16, 32):
+                nb = cus * per_cu
+
+                def run():
+                    st = L.peaks_stream(r, w, variant, vp(src.data_ptr() if src is not None else 0),
+                                        vp(dst.data_ptr() if dst is not None else 0), units,
+                                        vp(u32sink.data_ptr()), nb, sp)
+                    if st != 0:
+                        raise RuntimeError(f"peaks_stream: hip error {st}")
+
+                tt = timed(run, 5)
+                gbs = (r + w) * units * 16 / tt / 1e9
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "ms": tt * 1e3, "blocks": nb,
+                            "nontemporal": bool(variant & 1), "per_thread_step": 8 if variant & 2 else 4,
+                            "bytes_read": r * units * 16, "bytes_written": w * units * 16}
+        res[name] = best
+        log(f"[peaks] {name}: {best['GB/s']:.0f} GB/s ({best['blocks']} blocks)")
+        del src, dst
+        torch.cuda.empty_cache()
+    out["stream"] = res
+    return {"mode": "peaks", "metric": "achievable peaks (matrix-core loop, streaming kernels)", **out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -548,8 +698,9 @@ def main():
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "copy", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
+                    choices=["bench", "copy", "peaks", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
                     help="copy: run a plain device copy of known size (HBM counter calibration); "
+                         "peaks: achievable matrix-core and streaming peaks (libtrimul_peaks.so); "
                          "backward: the contraction step's gradients (trimul_tile_backward); "
                          "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward); "
                          "layer-backward: every gradient of the layer (the three backward entry points); "
@@ -580,6 +731,9 @@ def main():
     if args.mode == "atom-attention":
         print(json.dumps(bench_atom_attention(args, dev)), flush=True)
         return
+    if args.mode == "peaks":
+        print(json.dumps(bench_peaks(args, dev)), flush=True)
+        return
     work = wl.WORKLOADS[args.workload]
     if args.mode == "backward":
         print(json.dumps(bench_backward(work, args, dev)), flush=True)
@@ -592,6 +746,9 @@ def main():
         return
     if work.tile:
         print(json.dumps(bench_tile(work, args, dev)), flush=True)
+        return
+    if work.chunked:
+        print(json.dumps(bench_chunked(work, args, dev)), flush=True)
         return
     n = work.n
     log(f"[bench] generating {work.name} (N={n}) on the GPU")

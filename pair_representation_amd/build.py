@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtrimul.so")
+# measurement probes (matrix-core loop, streaming kernels): a library of their
+# own, loaded only by the benchmark's peaks mode
+PEAKS_LIB = os.path.join(PKG, "libtrimul_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 
 SOURCES = ["k1_project.hip", "k2_contract.hip", "k3_epilogue.hip", "k3b_epilogue_grad.hip", "kb_relayout.hip",
            "ka_window_attention.hip", "trimul_api.cpp"]
@@ -47,18 +51,23 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PEAKS_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PEAKS_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS_LIB)
     return LIB
 
 

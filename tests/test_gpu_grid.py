@@ -67,6 +67,23 @@ def test_grid_emulation_vs_oracle(case, direction):
 
 
 @pytest.mark.parametrize("direction", list(DIRS))
+@pytest.mark.parametrize("s_rows", [2, 3, 5])
+def test_row_block_mode_vs_oracle(case, direction, s_rows):
+    """The s x 1 split (output produced one row block at a time, each block's
+    k-blocks contracted in ring order) against the Q-mode oracle, not against
+    the library's own whole-grid path."""
+    n, z, mask, w, host = case
+    print(f"[case] grid {s_rows}x1 {direction} vs Q-oracle n={n}", flush=True)
+    emu = grid.emulate(z, mask, w, DIRS[direction], s_rows, 1)
+    torch.cuda.synchronize()
+    ref = oracle.trimul(host["z"], host["mask"], host["w"], direction, quant=True)
+    e = rel_err(emu.double().cpu().numpy(), ref)
+    print(f"  vs Q-oracle {e:.3e}", flush=True)
+    assert e <= 1e-2
+    assert (emu[~mask.bool()] == 0).all()
+
+
+@pytest.mark.parametrize("direction", list(DIRS))
 @pytest.mark.parametrize("s_rows,s_cols", [(2, 2), (3, 2), (3, 1)])
 def test_grid_backward_matches_oracle(dev, direction, s_rows, s_cols):
     """The grid's backward (grid.emulate_backward: each tile's share from the

@@ -130,6 +130,30 @@ def test_transpose_relation_on_gpu(dev):
 # kernel-level checks
 # ---------------------------------------------------------------------------
 
+def _one_flip_bound(h, side, direction):
+    """[c][rows][cols] bound on how far one bf16 rounding flip of one channel
+    of the normalised input zh moves the gated operand (before its own
+    rounding), in the operand plane's orientation: for each pair and output
+    channel d, max over input channels e of (|W_p[d,e]| + |u_d| / 4 *
+    |W_g[d,e]|) * ulp_bf16(zh_e), with u = W_p zh the projection and 1/4 the
+    largest slope of the logistic function."""
+    w = h["w"]
+    zh = oracle.bf16_round(oracle.layer_norm(h["z"], w["ln_in_w"], w["ln_in_b"]))
+    ulp_zh = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(zh), 2.0 ** -126))) - 7)
+    wp, wg = np.abs(w[f"w_{side}_proj"]), np.abs(w[f"w_{side}_gate"])
+    u = np.abs(zh @ w[f"w_{side}_proj"].T)
+    n = zh.shape[0]
+    out = np.empty(zh.shape[:2] + (wp.shape[0],))
+    for i in range(n):
+        for j0 in range(0, n, 32):
+            ue = ulp_zh[i, j0:j0 + 32, None, :]                   # [pairs, 1, e]
+            out[i, j0:j0 + 32] = (np.max(wp[None] * ue, axis=-1)
+                                  + u[i, j0:j0 + 32] / 4 * np.max(wg[None] * ue, axis=-1))
+    if direction == "incoming":
+        out = np.swapaxes(out, 0, 1)
+    return np.moveaxis(out, 2, 0)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("direction", DIRS)
 def test_operand_planes(dev, dtype, direction):
@@ -150,24 +174,33 @@ def test_operand_planes(dev, dtype, direction):
         m = h["mask"]
     ref_a = np.moveaxis(qa, 2, 0)   # [c][r][t]
     ref_b = np.moveaxis(qb, 2, 0)
-    for got, ref in ((a[:, :, :n], ref_a), (b[:, :, :n], ref_b)):
+    flip = {}
+    if dtype == "bf16":
+        flip["a"], flip["b"] = (_one_flip_bound(h, side, direction) for side in ("a", "b"))
+    for side, got, ref in (("a", a[:, :, :n], ref_a), ("b", b[:, :, :n], ref_b)):
         if dtype == "bf16":
-            # Both sides round to bf16 values computed along different paths
-            # (fp32 on the GPU, float64 in the oracle) whose pre-rounding
-            # difference is far below one bf16 ulp: almost every element is
-            # bit-identical and the rest differ by one or two ulps.
-            # A one-ulp flip of one normalised input channel moves the
-            # pre-rounding projection by up to max|W| * ulp(max|zh|), a few
-            # 1e-3 absolute; hence the absolute slack of 5% of rms.
-            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
-            rms = np.sqrt(np.mean(ref * ref))
+            # Both sides round to bf16 along different paths (fp32 on the GPU,
+            # float64 in the oracle).  Where the normalised input zh_e lies
+            # within fp32 error of a bf16 rounding midpoint the two roundings
+            # of zh_e differ by one ulp, which moves the pre-rounding operand
+            # by at most delta = max_e (|W_p[d,e]| + |u_d| / 4 |W_g[d,e]|)
+            # ulp(zh_e) (projection u and gate, sigma' <= 1/4); two such flips
+            # in one pair are allowed.  The final rounding of a and b then
+            # adds at most one ulp of the result.  A flip needs zh_e within a
+            # few fp32 ulps (2^-24 relative) of a midpoint, 2^-16 of the bf16
+            # spacing: of 128 channels per pair, about 128 * 2^-15 = 0.4% of
+            # the pairs hold one, so at most 1% of the elements may lie beyond
+            # one ulp and at least 98% must be bit-identical.
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(ref), np.abs(got)), 2.0 ** -126))) - 7)
             diff = np.abs(got - ref)
+            bound = ulp + 2.0 * flip[side]
             same = np.mean(got == ref)
-            over = np.mean(diff > 2 * ulp)
-            print(f"  bit-identical {same:.5f}, beyond 2 ulp {over:.2e}, max diff {diff.max():.3e}, "
-                  f"rms {rms:.3e}")
-            assert np.all(diff <= 2 * ulp + 0.05 * rms)
-            assert same > 0.98
+            beyond = np.mean(diff > ulp)
+            print(f"  {side}: bit-identical {same:.5f}, beyond 1 ulp {beyond:.2e}, max diff {diff.max():.3e}, "
+                  f"max bound {bound.max():.3e}, worst diff/bound {np.max(diff / bound):.3f}")
+            assert np.all(diff <= bound)
+            assert beyond <= 1e-2
+            assert same >= 0.98
         else:
             assert rel_err(got, ref) <= F32_TOL
     assert np.all(a[:, :, n:] == 0) and np.all(b[:, :, n:] == 0)
