@@ -132,20 +132,59 @@ typedef struct {
  * bytes.  Returns 0 for an invalid w or n. */
 size_t trimul_workspace_bytes(const trimul_weights_t *w, int64_t n);
 
-/* The full update over an n x n pair grid, outgoing direction.
+/* The full update over an n x n pair grid, outgoing direction: the layer that
+ * page 1 builds as TriangleMultiplicationOutgoing(size_input_embed) and calls
+ * as layer(x, mask) (section "Exemplo de codigo: triangle multiplication
+ * CP-aware"), on one device that holds the whole grid.
  *   z    : [n][n][c_z] in w->dtype, pair-major (channels contiguous)
  *   mask : [n][n] uint8, nonzero = keep the pair
  *   out  : [n][n][c_z] fp32, fully overwritten (zeros at masked pairs)
  *   workspace : >= trimul_workspace_bytes(w, n) bytes, 256-byte aligned;
- *               contents on entry are ignored, on return unspecified. */
+ *               contents on entry are ignored, on return unspecified.
+ * Errors: TRIMUL_ERR_INVALID_ARG (NULL pointer, n outside [0, 65535]),
+ * TRIMUL_ERR_UNSUPPORTED / _ALIGNMENT / _WORKSPACE_TOO_SMALL as named, all
+ * detected before anything is enqueued; TRIMUL_ERR_HIP if a launch fails. */
 trimul_status_t trimul_outgoing(const trimul_weights_t *w, const void *z, const uint8_t *mask,
                                 float *out, int64_t n, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
-/* The same for the incoming direction (x_ij = sum_k a_ki * b_kj). */
+/* The same for the incoming direction (x_ij = sum_k a_ki * b_kj), the
+ * layer's other orientation (page 1, section "Exemplo de codigo: triangle
+ * multiplication CP-aware", where the direction is the wrapper's parameter);
+ * arguments, ownership and errors as trimul_outgoing. */
 trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const uint8_t *mask,
                                 float *out, int64_t n, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* Bytes of workspace trimul_forward_chunked needs: with R = row_block,
+ * C = col_block, K = k_block (each 0 or > n meaning n),
+ *   align256(c * round_up(R, 256) * round_up(K, 64) * elt)      a chunk
+ * + align256(c * round_up(C, 256) * round_up(K, 64) * elt)      b chunk
+ * + align256(c * round_up(R, 4) * round_up(C, 16) * 4)           tile accumulator
+ * (elt = 2 for bf16, 4 for fp32; c = 128).  Returns 0 for an invalid w, n or
+ * a negative block. */
+size_t trimul_chunked_workspace_bytes(const trimul_weights_t *w, int64_t n, int64_t row_block,
+                                      int64_t col_block, int64_t k_block);
+
+/* The full update of trimul_outgoing / trimul_incoming (dir selects) in
+ * bounded device memory: the in-architecture chunking that page 1 names as
+ * the single-GPU workaround for pair grids beyond one device's memory
+ * (section "O problema dos workarounds atuais").  The output is produced one
+ * R x C tile at a time (row-major tile order); for each tile the k range is
+ * streamed in chunks of K residues: the chunk's a and b operands are built
+ * (input LayerNorm, gated projections, mask) and contracted into the tile's
+ * fp32 accumulator, and after the last chunk the epilogue writes the tile
+ * into out.  Besides z, mask and out, device memory is the workspace only
+ * (trimul_chunked_workspace_bytes), independent of n when R, C and K are
+ * fixed.  The a operand of a tile is rebuilt for every column tile and the b
+ * operand for every row tile, so the projection work grows as n/C + n/R.
+ * Arguments as trimul_outgoing plus dir and the three block sizes (>= 0;
+ * 0 = n); errors as trimul_outgoing.  Results agree with trimul_outgoing /
+ * trimul_incoming up to the fp32 summation order over k. */
+trimul_status_t trimul_forward_chunked(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                       const uint8_t *mask, float *out, int64_t n, int64_t row_block,
+                                       int64_t col_block, int64_t k_block, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Bytes of one operand buffer of trimul_tile_operands:
  * c * round_up(rows, 256) * ld * elt. */

@@ -9,6 +9,8 @@ is no fallback.  If the library has not been built, the first call raises.
 Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     workspace_bytes(w, n)
     outgoing(z, mask, w, ...), incoming(z, mask, w, ...)
+    chunked_workspace_bytes(w, n, row_block, col_block, k_block)
+    forward_chunked(z, mask, w, direction, row_block, col_block, k_block, ...)
     tile_operand_bytes(w, rows, ld)
     tile_operands(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, ...)
     tile(w, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z, mask, out_tile)
@@ -101,6 +103,10 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [W, vp, vp, vp, i64, vp, sz, vp]
             f.restype = ctypes.c_int
+        L.trimul_chunked_workspace_bytes.argtypes = [W, i64, i64, i64, i64]
+        L.trimul_chunked_workspace_bytes.restype = sz
+        L.trimul_forward_chunked.argtypes = [W, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.trimul_forward_chunked.restype = ctypes.c_int
         L.trimul_tile_operand_bytes.argtypes = [W, i64, i64]
         L.trimul_tile_operand_bytes.restype = sz
         L.trimul_tile_xacc_bytes.argtypes = [W, i64, i64]
@@ -235,6 +241,31 @@ def outgoing(z, mask, w: Weights, workspace=None, out=None):
 def incoming(z, mask, w: Weights, workspace=None, out=None):
     """out_ij = update with x_ij = sum_k a_ki * b_kj; returns fp32 [n, n, 128]."""
     return _full(lib().trimul_incoming, z, mask, w, workspace, out)
+
+
+def chunked_workspace_bytes(w: Weights, n: int, row_block: int = 0, col_block: int = 0, k_block: int = 0) -> int:
+    return int(lib().trimul_chunked_workspace_bytes(w.ref, n, row_block, col_block, k_block))
+
+
+def forward_chunked(z, mask, w: Weights, direction: int, row_block: int = 0, col_block: int = 0, k_block: int = 0,
+                    workspace=None, out=None):
+    """The update (direction OUTGOING or INCOMING) in bounded device memory:
+    R x C output tiles, each contracting k in chunks of K (0 = n); the
+    workspace holds one tile's operands and accumulator
+    (chunked_workspace_bytes).  Returns fp32 [n, n, 128]."""
+    n = z.shape[0]
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    if out is None:
+        out = torch.empty((n, n, C_Z), dtype=torch.float32, device=z.device)
+    _need(out, "out", torch.float32, (n, n, C_Z))
+    if workspace is None:
+        nb = chunked_workspace_bytes(w, n, row_block, col_block, k_block)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=z.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib().trimul_forward_chunked(w.ref, direction, _ptr(z), _ptr(mask), _ptr(out), n, row_block, col_block,
+                                        k_block, _ptr(workspace), workspace.numel(), _stream()))
+    return out
 
 
 def operand_shape(rows, ld):

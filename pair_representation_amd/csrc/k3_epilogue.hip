@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // bytes) of the pair's output row.
     const int64_t r = blk * 4 + (pq & 3), col = s0 + (pq >> 2);
     if (r < p.n_rows && col < p.n_cols) {
-      float *const orow = p.out + (r * p.n_cols + col) * kCz + o0;
+      float *const orow = p.out + (r * p.out_ld + col) * kCz + o0;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 v;

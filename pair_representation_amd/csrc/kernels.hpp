@@ -63,7 +63,8 @@ struct K3Args {
   const uint8_t *mask;    // [n][n] global
   int64_t n;
   int64_t row_off, n_rows, col_off, n_cols;
-  float *out;             // [n_rows][n_cols][c_z]
+  float *out;             // [n_rows][out_ld][c_z]: pair (r, s) of the tile at out + (r * out_ld + s) * c_z
+  int64_t out_ld;         // pairs between consecutive tile rows of out (>= n_cols)
   const float *ln_out_w, *ln_out_b, *ln_in_w, *ln_in_b;
   float eps;
   const void *w_out_proj;  // [c_z][c]

@@ -118,6 +118,7 @@ trimul::K3Args k3_args(const trimul_weights_t *w, const float *x, int64_t ldx, c
   a.col_off = col_off;
   a.n_cols = n_cols;
   a.out = out;
+  a.out_ld = n_cols;
   a.ln_out_w = w->ln_out_w;
   a.ln_out_b = w->ln_out_b;
   a.ln_in_w = w->ln_in_w;
@@ -178,6 +179,42 @@ trimul_status_t hip_fail(hipError_t e, const char *what) {
   return fail(TRIMUL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// K1 launches for one operand chunk (arguments already validated): one
+// launch writes both operands when their source rows coincide, else one per
+// requested operand.
+hipError_t enqueue_operands(const trimul_weights_t *w, trimul_dir_t dir, const void *z, const uint8_t *mask,
+                            int64_t n, int64_t row_off, int64_t n_rows, int64_t col_off, int64_t n_cols,
+                            int64_t k_off, int64_t k_len, int64_t ld, void *a_out, void *b_out, hipStream_t s) {
+  trimul::K1Args k1 = k1_args(w, z, mask, n);
+  k1.k_off = k_off;
+  k1.k_len = k_len;
+  k1.ld = ld;
+  k1.transposed = dir == TRIMUL_INCOMING ? 1 : 0;
+  if (a_out && b_out && row_off == col_off && n_rows == n_cols) {
+    k1.row_base = row_off;
+    k1.n_rows = n_rows;
+    k1.a_out = a_out;
+    k1.b_out = b_out;
+    return trimul::launch_k1(k1, w->dtype, s);
+  }
+  if (a_out) {
+    k1.row_base = row_off;
+    k1.n_rows = n_rows;
+    k1.a_out = a_out;
+    k1.b_out = nullptr;
+    const hipError_t e = trimul::launch_k1(k1, w->dtype, s);
+    if (e != hipSuccess) return e;
+  }
+  if (b_out) {
+    k1.row_base = col_off;
+    k1.n_rows = n_cols;
+    k1.a_out = nullptr;
+    k1.b_out = b_out;
+    return trimul::launch_k1(k1, w->dtype, s);
+  }
+  return hipSuccess;
+}
+
 trimul_status_t run_full(const trimul_weights_t *w, const void *z, const uint8_t *mask, float *out,
                          int64_t n, void *workspace, size_t workspace_bytes, void *stream,
                          bool incoming) {
@@ -231,6 +268,83 @@ trimul_status_t run_full(const trimul_weights_t *w, const void *z, const uint8_t
   return ok();
 }
 
+// Blocks of the memory-bounded forward: rows R, columns C and k-chunk K of
+// each step (0 or anything above n means n), and the workspace that holds
+// one step: the a operand of R rows, the b operand of C rows (both with row
+// length round_up(K, 64)) and the fp32 accumulator of an R x C tile.
+struct ChunkedLayout {
+  int64_t R, C, K, ldk;
+  size_t a_off, b_off, x_off, total;
+};
+
+ChunkedLayout chunked_layout(int32_t dtype, int64_t n, int64_t row_block, int64_t col_block, int64_t k_block) {
+  ChunkedLayout L;
+  L.R = (row_block <= 0 || row_block > n) ? n : row_block;
+  L.C = (col_block <= 0 || col_block > n) ? n : col_block;
+  L.K = (k_block <= 0 || k_block > n) ? n : k_block;
+  L.ldk = round_up(L.K, kKTile);
+  L.a_off = 0;
+  L.b_off = align256(operand_bytes(L.R, L.ldk, dtype));
+  L.x_off = L.b_off + align256(operand_bytes(L.C, L.ldk, dtype));
+  L.total = L.x_off + align256(xacc_bytes(L.R, L.C));
+  return L;
+}
+
+trimul_status_t check_full_args(const trimul_weights_t *w, const void *z, const uint8_t *mask, float *out,
+                                int64_t n, void *workspace) {
+  trimul_status_t st = check_weights(w);
+  if (st != TRIMUL_OK) return st;
+  if (n < 0 || n > kMaxN) return fail(TRIMUL_ERR_INVALID_ARG, "n=%lld out of range [0, %lld]", (long long)n, (long long)kMaxN);
+  if (n == 0) return TRIMUL_OK;
+  if (!z || !mask || !out) return fail(TRIMUL_ERR_INVALID_ARG, "z, mask and out must be non-NULL");
+  if (!workspace) return fail(TRIMUL_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(z, 16) || !aligned(out, 16)) return fail(TRIMUL_ERR_ALIGNMENT, "z and out must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TRIMUL_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  return TRIMUL_OK;
+}
+
+// The update one R x C output tile at a time; inside a tile the k range is
+// walked in chunks of K: the chunk's operands (K1), then the contraction
+// into the tile's accumulator (K2; the first chunk overwrites, the others
+// add), and after the last chunk the epilogue (K3) writes the tile straight
+// into out (row stride n).
+trimul_status_t enqueue_chunked(const trimul_weights_t *w, trimul_dir_t dir, const void *z, const uint8_t *mask,
+                                float *out, int64_t n, const ChunkedLayout &L, char *ws, hipStream_t s) {
+  void *a_buf = ws + L.a_off;
+  void *b_buf = ws + L.b_off;
+  float *x = reinterpret_cast<float *>(ws + L.x_off);
+  hipError_t e;
+  for (int64_t r0 = 0; r0 < n; r0 += L.R) {
+    const int64_t nr = std::min(L.R, n - r0);
+    for (int64_t c0 = 0; c0 < n; c0 += L.C) {
+      const int64_t nc = std::min(L.C, n - c0);
+      for (int64_t k0 = 0; k0 < n; k0 += L.K) {
+        const int64_t kl = std::min(L.K, n - k0);
+        e = enqueue_operands(w, dir, z, mask, n, r0, nr, c0, nc, k0, kl, L.ldk, a_buf, b_buf, s);
+        if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        trimul::K2Args k2{};
+        k2.ch[0].a = a_buf;
+        k2.ch[0].b = b_buf;
+        k2.ch[0].ld = L.ldk;
+        k2.ch[0].k_len = kl;
+        k2.n_chunks = 1;
+        k2.accumulate = k0 == 0 ? 0 : 1;
+        k2.M = nr;
+        k2.N = nc;
+        k2.x = x;
+        k2.ldx = x_ld(nc);
+        e = trimul::launch_k2(k2, w->dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "contraction kernel launch");
+      }
+      trimul::K3Args k3 = k3_args(w, x, x_ld(nc), z, mask, n, r0, nr, c0, nc, out + (r0 * n + c0) * 128);
+      k3.out_ld = n;
+      e = trimul::launch_k3(k3, w->dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "epilogue kernel launch");
+    }
+  }
+  return ok();
+}
+
 }  // namespace
 
 namespace trimul {
@@ -271,6 +385,30 @@ trimul_status_t trimul_incoming(const trimul_weights_t *w, const void *z, const 
   return run_full(w, z, mask, out, n, workspace, workspace_bytes, stream, true);
 }
 
+size_t trimul_chunked_workspace_bytes(const trimul_weights_t *w, int64_t n, int64_t row_block, int64_t col_block,
+                                      int64_t k_block) {
+  if (!w || (w->dtype != TRIMUL_F32 && w->dtype != TRIMUL_BF16) || n < 1 || n > kMaxN) return 0;
+  if (row_block < 0 || col_block < 0 || k_block < 0) return 0;
+  return chunked_layout(w->dtype, n, row_block, col_block, k_block).total;
+}
+
+trimul_status_t trimul_forward_chunked(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                       const uint8_t *mask, float *out, int64_t n, int64_t row_block,
+                                       int64_t col_block, int64_t k_block, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  trimul_status_t st = check_full_args(w, z, mask, out, n, workspace);
+  if (st != TRIMUL_OK) return st;
+  if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING) return fail(TRIMUL_ERR_INVALID_ARG, "unknown direction %d", (int)dir);
+  if (row_block < 0 || col_block < 0 || k_block < 0)
+    return fail(TRIMUL_ERR_INVALID_ARG, "block sizes must be >= 0 (0 = n): %lld %lld %lld", (long long)row_block,
+                (long long)col_block, (long long)k_block);
+  if (n == 0) return ok();
+  const ChunkedLayout L = chunked_layout(w->dtype, n, row_block, col_block, k_block);
+  if (workspace_bytes < L.total)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  return enqueue_chunked(w, dir, z, mask, out, n, L, static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
 size_t trimul_tile_xacc_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols) {
   if (!w || n_rows < 0 || n_cols < 0) return 0;
   return xacc_bytes(n_rows, n_cols);
@@ -302,39 +440,9 @@ trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir
   if (!aligned(z, 16) || (a_out && !aligned(a_out, 16)) || (b_out && !aligned(b_out, 16)))
     return fail(TRIMUL_ERR_ALIGNMENT, "z, a_out and b_out must be 16-byte aligned");
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  trimul::K1Args k1 = k1_args(w, z, mask, n);
-  k1.k_off = k_off;
-  k1.k_len = k_len;
-  k1.ld = ld;
-  k1.transposed = dir == TRIMUL_INCOMING ? 1 : 0;
-  const bool shared_rows = a_out && b_out && row_off == col_off && n_rows == n_cols;
-  hipError_t e;
-  if (shared_rows) {
-    k1.row_base = row_off;
-    k1.n_rows = n_rows;
-    k1.a_out = a_out;
-    k1.b_out = b_out;
-    e = trimul::launch_k1(k1, w->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
-    return ok();
-  }
-  if (a_out) {
-    k1.row_base = row_off;
-    k1.n_rows = n_rows;
-    k1.a_out = a_out;
-    k1.b_out = nullptr;
-    e = trimul::launch_k1(k1, w->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
-  }
-  if (b_out) {
-    k1.row_base = col_off;
-    k1.n_rows = n_cols;
-    k1.a_out = nullptr;
-    k1.b_out = b_out;
-    e = trimul::launch_k1(k1, w->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
-  }
+  hipError_t e = enqueue_operands(w, dir, z, mask, n, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, a_out,
+                                  b_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
   return ok();
 }
 

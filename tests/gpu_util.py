@@ -37,3 +37,24 @@ def sample_indices(n, seed, count=48, must=()):
     while len(s) < min(count, n):
         s.add(int(r.integers(0, n)))
     return np.array(sorted(s))
+
+
+def whole_tensor_checks(out, mask_dev, sample_out, sample_mask, rows_per_step=512):
+    """Finite everywhere, exact zeros at masked pairs, and the rms over kept
+    pairs within 5% of the sample's rms over its kept pairs; the output is
+    scanned in row blocks so no temporary of its full size is made."""
+    sq = 0.0
+    kept = 0
+    for r0 in range(0, out.shape[0], rows_per_step):
+        o = out[r0:r0 + rows_per_step]
+        assert bool(torch.isfinite(o).all())
+        m = mask_dev[r0:r0 + rows_per_step] != 0
+        if bool((~m).any()):
+            assert torch.count_nonzero(o[~m]).item() == 0
+        sq += torch.sum(o[m].double() ** 2).item()
+        kept += int(m.sum().item()) * o.shape[-1]
+    rms_full = (sq / kept) ** 0.5
+    s = sample_out[np.asarray(sample_mask) != 0]
+    rms_s = float(np.sqrt(np.mean(s ** 2)))
+    print(f"  rms over kept pairs: full {rms_full:.4f} sample {rms_s:.4f}")
+    assert abs(rms_full / rms_s - 1) < 0.05

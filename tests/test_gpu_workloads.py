@@ -19,7 +19,7 @@ import torch
 import oracle
 import pair_representation_amd as pra
 import workloads as wl
-from tests.gpu_util import device_getters, rel_err, sample_indices
+from tests.gpu_util import device_getters, rel_err, sample_indices, whole_tensor_checks as _whole_tensor_checks
 
 pytestmark = pytest.mark.gpu
 
@@ -42,26 +42,6 @@ def _free():
 def _weights(work, dev):
     wts = wl.make_weights(work.c_z, work.c, work.seed, work.dtype)
     return pra.Weights(wts, pra.BF16 if work.dtype == "bf16" else pra.F32, device=dev), wl.weights_f64(wts)
-
-
-def _whole_tensor_checks(out, mask_dev, sample_out, sample_mask):
-    """Finite everywhere, exact zeros at masked pairs, and the rms over kept
-    pairs within 5% of the sample's rms over its kept pairs."""
-    assert bool(torch.isfinite(out).all())
-    sq = 0.0
-    kept = 0
-    for r0 in range(0, out.shape[0], 512):
-        o = out[r0:r0 + 512]
-        m = mask_dev[r0:r0 + 512] != 0
-        if bool((~m).any()):
-            assert torch.count_nonzero(o[~m]).item() == 0
-        sq += torch.sum(o[m].double() ** 2).item()
-        kept += int(m.sum().item()) * o.shape[-1]
-    rms_full = (sq / kept) ** 0.5
-    s = sample_out[np.asarray(sample_mask) != 0]
-    rms_s = float(np.sqrt(np.mean(s ** 2)))
-    print(f"  rms over kept pairs: full {rms_full:.4f} sample {rms_s:.4f}")
-    assert abs(rms_full / rms_s - 1) < 0.05
 
 
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])

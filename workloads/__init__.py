@@ -22,6 +22,12 @@ Workloads (sizes from the pages, values synthetic):
                      da pair representation", split 2 x 2: one device's tile
                      is rows 0-4999 x cols 0-4999, and its k-contraction
                      streams in 8 chunks of 1250 residues.
+* ``n14000_chunked`` -- N=14000, a grid whose whole-grid workspace does not
+                     fit beside z and the output on one device (page 1's
+                     "O problema dos workarounds atuais": chunking is the
+                     single-GPU workaround); run in the memory-bounded form
+                     with 3500-row output blocks at full width and k in two
+                     chunks of 7000; 2% random residues masked out.
 
 Every workload uses c_z = c = 128, z ~ N(0, 1), Xavier-normal weights (one
 draw per logical matrix), LayerNorm gamma = 1 and beta = 0.
@@ -60,6 +66,7 @@ class Workload:
     pad_fraction: float = 0.0       # trailing residues with mask 0
     masked_fraction: float = 0.0    # random residues with mask 0
     tile: dict = field(default_factory=dict)  # tiled form: rows, cols, chunk, n_chunks
+    chunked: dict = field(default_factory=dict)  # memory-bounded form: row_block, col_block, k_block
 
 
 WORKLOADS = {
@@ -72,6 +79,8 @@ WORKLOADS = {
     "n10000_tile": Workload("n10000_tile", 10000, "bf16", seed=5,
                             tile={"row_off": 0, "n_rows": 5000, "col_off": 0, "n_cols": 5000,
                                   "chunk": 1250, "n_chunks": 8}),
+    "n14000_chunked": Workload("n14000_chunked", 14000, "bf16", seed=6, masked_fraction=0.02,
+                               chunked={"row_block": 3500, "col_block": 0, "k_block": 7000}),
 }
 
 
