@@ -125,7 +125,9 @@ typedef struct {
   const void *b;
 } trimul_kchunk_t;
 
-/* Bytes of workspace trimul_outgoing / trimul_incoming need for size n: the
+/* Bytes of workspace trimul_outgoing / trimul_incoming need for size n (the
+ * buffers between the three steps of the layer of page 1, section "Exemplo de
+ * codigo: triangle multiplication CP-aware"): the
  * a and b operands of all n rows with ld = round_up(n, 64) in the operand
  * layout of trimul_kchunk_t (element = dtype), and the fp32 contraction result
  * in the x_acc layout of trimul_tile for an n x n tile, each rounded up to 256
@@ -186,11 +188,15 @@ trimul_status_t trimul_forward_chunked(const trimul_weights_t *w, trimul_dir_t d
                                        int64_t col_block, int64_t k_block, void *workspace,
                                        size_t workspace_bytes, void *stream);
 
-/* Bytes of one operand buffer of trimul_tile_operands:
+/* Bytes of one operand buffer of trimul_tile_operands (one ring message of
+ * page 1, section "Sobreposicao de computacao e comunicacao"):
  * c * round_up(rows, 256) * ld * elt. */
 size_t trimul_tile_operand_bytes(const trimul_weights_t *w, int64_t rows, int64_t ld);
 
-/* The operand chunk a device owning z contributes for one tile: runs the
+/* The operand chunk a device owning z contributes for one tile (page 1,
+ * section "2D tiling da pair representation": each device holds one block of
+ * the pair grid; section "Sobreposicao de computacao e comunicacao": the
+ * operand blocks travel around the row or column ring): runs the
  * input LayerNorm, gated projections and mask on the source pairs and writes
  *   a_out[d][r][t] = operand a of (row_off + r, k_off + t),  r < n_rows
  *   b_out[d][s][t] = operand b of (col_off + s, k_off + t),  s < n_cols
@@ -204,11 +210,19 @@ trimul_status_t trimul_tile_operands(const trimul_weights_t *w, trimul_dir_t dir
                                      int64_t k_off, int64_t k_len, int64_t ld, void *a_out,
                                      void *b_out, void *stream);
 
-/* Bytes of the fp32 tile accumulator x_acc of trimul_tile:
+/* Bytes of the fp32 tile accumulator x_acc of trimul_tile (the contraction
+ * result of one device's tile, page 1, section "2D tiling da pair
+ * representation"):
  * c * round_up(n_rows, 4) * round_up(n_cols, 16) * 4. */
 size_t trimul_tile_xacc_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols);
 
-/* One device's tile of the pair grid: rows row_off .. row_off+n_rows-1, cols
+/* One device's tile of the pair grid (page 1, section "2D tiling da pair
+ * representation"), contracting the k-chunks in the order the ring delivers
+ * them while the next ones are in flight (section "Sobreposicao de computacao
+ * e comunicacao").  There is no direction argument: incoming operands arrive
+ * already transposed (trimul_tile_operands writes them so), which makes the
+ * contraction and the epilogue identical for both directions.
+ * Rows row_off .. row_off+n_rows-1, cols
  * col_off .. col_off+n_cols-1.  Contracts the given chunks (host array, in
  * arrival order) into the fp32 accumulator x_acc, stored in blocks of 4 rows
  * x 16 columns with the 128 channels of a block adjacent, so that the
