@@ -188,6 +188,38 @@ trimul_status_t trimul_forward_chunked(const trimul_weights_t *w, trimul_dir_t d
                                        int64_t col_block, int64_t k_block, void *workspace,
                                        size_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array that trimul_forward_chunked_noalloc uses
+ * in place of a workspace argument (256 MiB). */
+#define TRIMUL_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* trimul_forward_chunked without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace lives in a
+ * library-owned device array of TRIMUL_NOALLOC_SCRATCH_BYTES: one copy per
+ * device, created when the library's code is first loaded on that device
+ * and held until the process ends.  Its device address is looked up once per
+ * device on the first call made with that device current.  Nothing is
+ * allocated or freed by the call (no hipMalloc / hipFree, no allocating
+ * library routine).
+ *   Blocks as trimul_forward_chunked; trimul_chunked_workspace_bytes(w, n,
+ *   row_block, col_block, k_block) must not exceed
+ *   TRIMUL_NOALLOC_SCRATCH_BYTES, else TRIMUL_ERR_WORKSPACE_TOO_SMALL (with a
+ *   message naming both sizes) and nothing is enqueued.  With all blocks 0
+ *   that is the whole-grid workspace: n <= 512 (bf16) or n <= 356 (fp32);
+ *   e.g. 512 x 512 x 512 (bf16) or 512 x 512 x 256 (fp32) blocks fit and
+ *   serve any n.
+ *   Results are bitwise those of trimul_forward_chunked with the same
+ *   blocks.  Every call on a device shares that device's array and leaves
+ *   its contents behind (no kernel reads scratch it has not written in the
+ *   same call): calls that overlap in time on one device (other streams,
+ *   other threads) race and must be serialized by the caller.
+ *   Errors: as trimul_forward_chunked; TRIMUL_ERR_HIP if the array's
+ *   address cannot be obtained. */
+trimul_status_t trimul_forward_chunked_noalloc(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                               const uint8_t *mask, float *out, int64_t n,
+                                               int64_t row_block, int64_t col_block, int64_t k_block,
+                                               void *stream);
+
 /* Bytes of one operand buffer of trimul_tile_operands (one ring message of
  * page 1, section "Sobreposicao de computacao e comunicacao"):
  * c * round_up(rows, 256) * ld * elt. */

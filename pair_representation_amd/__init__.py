@@ -11,6 +11,7 @@ Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     outgoing(z, mask, w, ...), incoming(z, mask, w, ...)
     chunked_workspace_bytes(w, n, row_block, col_block, k_block)
     forward_chunked(z, mask, w, direction, row_block, col_block, k_block, ...)
+    forward_chunked_noalloc(z, mask, w, direction, row_block, col_block, k_block, out=None)
     tile_operand_bytes(w, rows, ld)
     tile_operands(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, ...)
     tile(w, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z, mask, out_tile)
@@ -107,6 +108,8 @@ def lib():
         L.trimul_chunked_workspace_bytes.restype = sz
         L.trimul_forward_chunked.argtypes = [W, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.trimul_forward_chunked.restype = ctypes.c_int
+        L.trimul_forward_chunked_noalloc.argtypes = [W, ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, vp]
+        L.trimul_forward_chunked_noalloc.restype = ctypes.c_int
         L.trimul_tile_operand_bytes.argtypes = [W, i64, i64]
         L.trimul_tile_operand_bytes.restype = sz
         L.trimul_tile_xacc_bytes.argtypes = [W, i64, i64]
@@ -265,6 +268,26 @@ def forward_chunked(z, mask, w: Weights, direction: int, row_block: int = 0, col
     _need(workspace, "workspace", torch.uint8)
     _check(lib().trimul_forward_chunked(w.ref, direction, _ptr(z), _ptr(mask), _ptr(out), n, row_block, col_block,
                                         k_block, _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # TRIMUL_NOALLOC_SCRATCH_BYTES
+
+
+def forward_chunked_noalloc(z, mask, w: Weights, direction: int, row_block: int = 0, col_block: int = 0,
+                            k_block: int = 0, out=None):
+    """forward_chunked with the workspace in the library's device scratch
+    array (no allocation by the library; ``out`` is allocated here only when
+    not given).  The blocks' workspace must fit in NOALLOC_SCRATCH_BYTES.
+    Calls that overlap on one device race on the shared array."""
+    n = z.shape[0]
+    _need(z, "z", w.torch_dtype, (n, n, C_Z))
+    _need(mask, "mask", torch.uint8, (n, n))
+    if out is None:
+        out = torch.empty((n, n, C_Z), dtype=torch.float32, device=z.device)
+    _need(out, "out", torch.float32, (n, n, C_Z))
+    _check(lib().trimul_forward_chunked_noalloc(w.ref, direction, _ptr(z), _ptr(mask), _ptr(out), n, row_block,
+                                                col_block, k_block, _stream()))
     return out
 
 

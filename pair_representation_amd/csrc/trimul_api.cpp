@@ -345,6 +345,32 @@ trimul_status_t enqueue_chunked(const trimul_weights_t *w, trimul_dir_t dir, con
   return ok();
 }
 
+// Workspace of trimul_forward_chunked_noalloc: a file-scope device array, one
+// copy per device.  In host code its name is a host-side stand-in, not a
+// device address: only the address hipGetSymbolAddress returns (kept per
+// device below) is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[TRIMUL_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+trimul_status_t scratch_address(char **out) {
+  static std::mutex mu;
+  static std::vector<void *> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    addr[dev] = p;
+  }
+  *out = static_cast<char *>(addr[dev]);
+  return TRIMUL_OK;
+}
+
 }  // namespace
 
 namespace trimul {
@@ -407,6 +433,31 @@ trimul_status_t trimul_forward_chunked(const trimul_weights_t *w, trimul_dir_t d
   if (workspace_bytes < L.total)
     return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
   return enqueue_chunked(w, dir, z, mask, out, n, L, static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+trimul_status_t trimul_forward_chunked_noalloc(const trimul_weights_t *w, trimul_dir_t dir, const void *z,
+                                               const uint8_t *mask, float *out, int64_t n, int64_t row_block,
+                                               int64_t col_block, int64_t k_block, void *stream) {
+  // validation as trimul_forward_chunked, with the scratch array standing in
+  // for the workspace (any non-NULL, 256-byte aligned pointer passes the
+  // workspace checks)
+  const void *placeholder = reinterpret_cast<const void *>(uintptr_t(256));
+  trimul_status_t st = check_full_args(w, z, mask, out, n, const_cast<void *>(placeholder));
+  if (st != TRIMUL_OK) return st;
+  if (dir != TRIMUL_OUTGOING && dir != TRIMUL_INCOMING) return fail(TRIMUL_ERR_INVALID_ARG, "unknown direction %d", (int)dir);
+  if (row_block < 0 || col_block < 0 || k_block < 0)
+    return fail(TRIMUL_ERR_INVALID_ARG, "block sizes must be >= 0 (0 = n): %lld %lld %lld", (long long)row_block,
+                (long long)col_block, (long long)k_block);
+  if (n == 0) return ok();
+  const ChunkedLayout L = chunked_layout(w->dtype, n, row_block, col_block, k_block);
+  if (L.total > TRIMUL_NOALLOC_SCRATCH_BYTES)
+    return fail(TRIMUL_ERR_WORKSPACE_TOO_SMALL,
+                "blocks %lld x %lld x %lld need %zu bytes of workspace, more than the %zu-byte scratch array",
+                (long long)L.R, (long long)L.C, (long long)L.K, L.total, (size_t)TRIMUL_NOALLOC_SCRATCH_BYTES);
+  char *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TRIMUL_OK) return st;
+  return enqueue_chunked(w, dir, z, mask, out, n, L, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t trimul_tile_xacc_bytes(const trimul_weights_t *w, int64_t n_rows, int64_t n_cols) {

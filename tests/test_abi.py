@@ -162,6 +162,41 @@ def test_chunked_validation():
     assert str(need) in L.trimul_last_error().decode()
 
 
+def test_noalloc_validation():
+    """The allocation-free variant validates like trimul_forward_chunked and
+    rejects blocks whose workspace exceeds its scratch array, before any HIP
+    call (the array's address is looked up only after validation)."""
+    L = pra.lib()
+    text = open(HEADER).read()
+    m = re.search(r"#define TRIMUL_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pra.NOALLOC_SCRATCH_BYTES
+
+    def call(w=None, direction=pra.OUTGOING, n=300, blocks=(0, 0, 0), z=FAKE, mask=FAKE + 1, out=FAKE + 0x100000):
+        w = weights() if w is None else w
+        return L.trimul_forward_chunked_noalloc(ctypes.byref(w), direction, z, mask, out, n, *blocks, None)
+
+    assert call(n=0, z=None, mask=None, out=None) == pra.OK
+    assert call(w=weights(c=64)) == pra.ERR_UNSUPPORTED
+    assert call(direction=5) == pra.ERR_INVALID_ARG
+    assert call(blocks=(0, -1, 0)) == pra.ERR_INVALID_ARG
+    assert call(z=None) == pra.ERR_INVALID_ARG
+    assert call(out=FAKE + 0x100004) == pra.ERR_ALIGNMENT
+    assert call(n=70000) == pra.ERR_INVALID_ARG
+    # n = 600 in one block needs more than the array; bf16 n = 512 and fp32
+    # n = 356 are the largest whole-grid sizes that fit
+    w16, w32 = weights(pra.BF16), weights(pra.F32)
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w16), 512, 0, 0, 0) <= pra.NOALLOC_SCRATCH_BYTES
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w16), 513, 0, 0, 0) > pra.NOALLOC_SCRATCH_BYTES
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w32), 356, 0, 0, 0) <= pra.NOALLOC_SCRATCH_BYTES
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w32), 357, 0, 0, 0) > pra.NOALLOC_SCRATCH_BYTES
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w16), 65535, 512, 512, 512) <= pra.NOALLOC_SCRATCH_BYTES
+    assert L.trimul_chunked_workspace_bytes(ctypes.byref(w32), 65535, 512, 512, 256) <= pra.NOALLOC_SCRATCH_BYTES
+    assert call(n=600) == pra.ERR_WORKSPACE_TOO_SMALL
+    msg = L.trimul_last_error().decode()
+    assert str(pra.NOALLOC_SCRATCH_BYTES) in msg and "600 x 600 x 600" in msg
+    assert call(w=w32, n=2000, blocks=(512, 512, 512)) == pra.ERR_WORKSPACE_TOO_SMALL
+
+
 def call_ops(w=None, direction=pra.OUTGOING, z=FAKE, mask=FAKE, n=100, row_off=0, n_rows=10, col_off=0,
              n_cols=10, k_off=0, k_len=100, ld=128, a=FAKE + 0x10000000, b=FAKE + 0x20000000):
     w = weights() if w is None else w
