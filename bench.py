@@ -36,11 +36,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix peak (the fp32 path's contraction instructions)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 C = 128
 C_Z = 128
-K1_BYTES_PER_PAIR = 256 + 1 + 2 * C * 2        # z (bf16) + mask + a, b (bf16)
-K3_BYTES_PER_PAIR = C * 4 + 256 + 1 + C_Z * 4  # x (fp32) + z + mask + out (fp32)
+def k1_bytes_per_pair(elt):
+    """z in the storage type + mask + a, b in the storage type."""
+    return C_Z * elt + 1 + 2 * C * elt
+
+
+def k3_bytes_per_pair(elt):
+    """x (fp32) + z in the storage type + mask + out (fp32)."""
+    return C * 4 + C_Z * elt + 1 + C_Z * 4
+
+
+K1_BYTES_PER_PAIR = k1_bytes_per_pair(2)   # bf16: 769
+K3_BYTES_PER_PAIR = k3_bytes_per_pair(2)   # bf16: 1281
 K1_FLOPS_PER_PAIR = 4 * C * C_Z * 2
 K3_FLOPS_PER_PAIR = 2 * C_Z * C * 2
 
@@ -50,18 +61,34 @@ def log(*a):
 
 
 def traffic_from_profile(kernel_src):
-    """HBM bytes per contraction launch from the committed counter summary, or
-    None when the summary is absent or the kernel source changed since."""
+    """L2-miss bytes per contraction launch from the committed counter summary
+    (the L2's FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy; they
+    include reads served by the Infinity Cache, so they bound the DRAM traffic
+    from above), or None when the summary is absent or the kernel source
+    changed since."""
     path = os.path.join(ROOT, "profiles", "k2_contract_n3605_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"source sha256: ([0-9a-f]{64})", text)
-    m_b = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
+    m_b = re.search(r"L2-miss bytes per launch: ([0-9.eE+]+)", text)
     if not m_sha or not m_b:
         return None
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def measured_ceilings():
+    """Achievable peaks measured on this GPU model by the peaks mode (the
+    committed summary profiles/peaks_mi355x.md): the bf16 matrix-core loop and
+    the streaming kernels at the projection's and epilogue's byte mixes."""
+    path = os.path.join(ROOT, "profiles", "peaks_mi355x.md")
+    if not os.path.exists(path):
+        return {}
+    out = {}
+    for m in re.finditer(r"ceiling (\w+) (GB/s|TFLOP/s): ([0-9.]+)", open(path).read()):
+        out[m.group(1)] = float(m.group(3))
+    return out
 
 
 def blas_threads():
@@ -699,7 +726,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "copy", "peaks", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
-                    help="copy: run a plain device copy of known size (HBM counter calibration); "
+                    help="copy: a plain 1 GiB device copy by the streaming probe kernel (counter calibration); "
                          "peaks: achievable matrix-core and streaming peaks (libtrimul_peaks.so); "
                          "backward: the contraction step's gradients (trimul_tile_backward); "
                          "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward); "
@@ -719,14 +746,29 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.mode == "copy":
+        # a plain copy of known size through the streaming probe kernel of
+        # libtrimul_peaks.so (one 16-byte load and one 16-byte store per
+        # lane), for calibrating the FETCH_SIZE / WRITE_SIZE counters
+        import ctypes
+
+        from pair_representation_amd import build as pbuild
+        L = ctypes.CDLL(pbuild.PEAKS_LIB)
+        vp = ctypes.c_void_p
+        L.peaks_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_longlong, vp,
+                                   ctypes.c_int, vp]
         nbytes = 1 << 30
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
         for _ in range(3):
-            dst.copy_(src)
+            st = L.peaks_stream(1, 1, 0, vp(src.data_ptr()), vp(dst.data_ptr()), nbytes // 16, vp(sink.data_ptr()),
+                                cus * 8, vp(torch.cuda.current_stream(dev).cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"peaks_stream: hip error {st}")
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
-                          "launches": 3}), flush=True)
+        print(json.dumps({"mode": "copy", "kernel": "stream_rw<1, 1, 4, false>", "bytes_read_per_launch": nbytes,
+                          "bytes_written_per_launch": nbytes, "launches": 3}), flush=True)
         return
     if args.mode == "atom-attention":
         print(json.dumps(bench_atom_attention(args, dev)), flush=True)
@@ -827,9 +869,18 @@ def main():
     pairs = n * n
     k2_flops = 2.0 * n * n * n * C
     k2_tflops = k2_flops / avg["k2"] / 1e12
-    k1_gbs = K1_BYTES_PER_PAIR * pairs / avg["k1"] / 1e9
-    k3_gbs = K3_BYTES_PER_PAIR * pairs / avg["k3"] / 1e9
+    # the contraction's peak in its own arithmetic type
+    k2_peak = PEAK_BF16_TFLOPS if work.dtype == "bf16" else PEAK_FP32_TFLOPS
+    elt = 2 if work.dtype == "bf16" else 4
+    k1_bpp, k3_bpp = k1_bytes_per_pair(elt), k3_bytes_per_pair(elt)
+    k1_gbs = k1_bpp * pairs / avg["k1"] / 1e9
+    k3_gbs = k3_bpp * pairs / avg["k3"] / 1e9
     traffic = traffic_from_profile(os.path.join(ROOT, "pair_representation_amd", "csrc", "k2_contract.hip"))
+    ceil = measured_ceilings()
+
+    def vs_ceiling(rate, key):
+        return None if key not in ceil else {"ceiling": ceil[key], "frac_of_ceiling": rate / ceil[key],
+                                             "ceiling_source": f"profiles/peaks_mi355x.md ({key})"}
 
     value = 2 * pairs / t_api
     rec = {
@@ -847,27 +898,32 @@ def main():
         "data": "synthetic (seeded z ~ N(0,1) + inter-chain offset vectors, Xavier-normal weights)",
         "config": {"workload": work.name, "n": n, "c_z": C_Z, "c": C, "chains": list(work.chains),
                    "directions": ["outgoing", "incoming"], "pair_updates_per_step": 2 * pairs},
-        "mfma_util_pct": 100.0 * k2_tflops / PEAK_BF16_TFLOPS,
+        "mfma_util_pct": 100.0 * k2_tflops / k2_peak,
         "roofline": {
             "bound": "mfma",
             "kernel": "k2_contract (channel-batched k-contraction)",
             "achieved": k2_tflops,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": k2_peak,
             "unit": "TFLOP/s",
-            "frac": k2_tflops / PEAK_BF16_TFLOPS,
+            "frac": k2_tflops / k2_peak,
             "traffic": traffic,
+            "traffic_kind": "L2-miss (fabric) bytes per launch: L2 FETCH_SIZE and WRITE_SIZE calibrated on a plain "
+                            "copy; includes Infinity-Cache hits, so an upper bound on DRAM bytes",
             "algorithmic_per_launch": f"2*N^3*c = {k2_flops:.4e} flop",
             "avg_launch_ms": avg["k2"] * 1e3,
+            "vs_measured_mfma_loop": vs_ceiling(k2_tflops, "mfma_bf16"),
         },
         "kernels": {
             "k1_project": {"avg_ms": avg["k1"] * 1e3, "bound": "hbm", "GB/s": k1_gbs,
-                           "frac": k1_gbs / PEAK_HBM_GBS, "bytes_per_pair": K1_BYTES_PER_PAIR,
-                           "TFLOP/s": K1_FLOPS_PER_PAIR * pairs / avg["k1"] / 1e12},
+                           "frac": k1_gbs / PEAK_HBM_GBS, "bytes_per_pair": k1_bpp,
+                           "TFLOP/s": K1_FLOPS_PER_PAIR * pairs / avg["k1"] / 1e12,
+                           "vs_measured_stream": vs_ceiling(k1_gbs, "k1_mix_1r_2w")},
             "k2_contract": {"avg_ms": avg["k2"] * 1e3, "bound": "mfma", "TFLOP/s": k2_tflops,
-                            "frac": k2_tflops / PEAK_BF16_TFLOPS},
+                            "frac": k2_tflops / k2_peak},
             "k3_epilogue": {"avg_ms": avg["k3"] * 1e3, "bound": "hbm", "GB/s": k3_gbs,
-                            "frac": k3_gbs / PEAK_HBM_GBS, "bytes_per_pair": K3_BYTES_PER_PAIR,
-                            "TFLOP/s": K3_FLOPS_PER_PAIR * pairs / avg["k3"] / 1e12},
+                            "frac": k3_gbs / PEAK_HBM_GBS, "bytes_per_pair": k3_bpp,
+                            "TFLOP/s": K3_FLOPS_PER_PAIR * pairs / avg["k3"] / 1e12,
+                            "vs_measured_stream": vs_ceiling(k3_gbs, "k3_mix_3r_2w")},
             "per_kernel_loop_ms_per_step": t_kern * 1e3,
         },
         "per_direction": per_dir,

@@ -1,7 +1,8 @@
-"""Host-side logic of bench.py (no GPU): the one-GPU guard, the HBM traffic
-figure read from the committed counter summary (and dropped once the
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the L2-miss
+traffic figure read from the committed counter summary (and dropped once the
 contraction kernel's source differs from the one the counters were taken
-on), and the oracle host description."""
+on), the measured ceilings read from the committed peaks summary, the
+bytes-per-pair figures per storage type, and the oracle host description."""
 
 import os
 import shutil
@@ -41,3 +42,15 @@ def test_host_description():
     assert h["os_cpu_count"] == os.cpu_count()
     assert h["usable_cpus"] is None or 1 <= h["usable_cpus"] <= os.cpu_count()
     assert bench.blas_threads() >= 1
+
+
+def test_measured_ceilings_and_bytes_per_pair():
+    c = bench.measured_ceilings()
+    # a matrix-core loop near the published 2.5 PFLOP/s; streaming rates
+    # below the published 8 TB/s
+    assert 2000 < c["mfma_bf16"] <= 2520
+    for k in ("k1_mix_1r_2w", "k3_mix_3r_2w", "copy"):
+        assert 3000 < c[k] < 8000
+    # bf16: z 256 + mask 1 + a, b 512; fp32 doubles the z and operand bytes
+    assert bench.k1_bytes_per_pair(2) == 769 and bench.k1_bytes_per_pair(4) == 1537
+    assert bench.k3_bytes_per_pair(2) == 1281 and bench.k3_bytes_per_pair(4) == 1537
