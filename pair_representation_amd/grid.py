@@ -20,8 +20,11 @@ send) and contracted by one trimul_tile call (FIRST on the first block, LAST on
 the final one), exactly as a device would do it; the only other step is
 placing each tile of the result into the full output.
 
-An s x 1 split is the memory-bounded mode: the output is produced in row
-blocks, and the contraction result is held for one block at a time.
+An s x 1 split produces the output in row blocks with one block's contraction
+result resident; it still builds a full-height b operand per block.  The
+memory-bounded forward proper, which bounds a, b and the accumulator by
+tiling the output in both directions and streaming k in chunks, is the
+library's trimul_forward_chunked (binding: forward_chunked).
 
 emulate_backward runs the same grid's backward (the training step the pages
 make the point of the tiling): each tile's gradients from the library's three
