@@ -73,7 +73,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // order, so all 16 lanes receive bit-identical totals.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]

@@ -183,21 +183,28 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
     const int64_t j = p.transposed ? p.row_base + rr : p.k_off + tt;
     return i * p.n + j;
   };
-  // pair offsets of this thread's two units from the item's first pair
+  // offsets of this thread's two units from the item's first pair
   // (consecutive plane columns are consecutive pairs, or pairs n apart when
-  // the plane is transposed); used for items that lie wholly in range
-  int64_t poff[2];
+  // the plane is transposed), in pairs (mask) and in bytes (z); used for
+  // items that lie wholly in range, addressed as a wave-uniform base plus
+  // these loop-invariant 32-bit offsets (at most 63 * 65535 pairs of 512
+  // bytes, below 2^32)
+  uint32_t poff[2], zoff[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) poff[s] = (int64_t)(32 * s + (tid >> 4)) * (p.transposed ? p.n : 1);
+  for (int s = 0; s < 2; ++s) {
+    poff[s] = (uint32_t)(32 * s + (tid >> 4)) * (uint32_t)(p.transposed ? p.n : 1);
+    zoff[s] = (poff[s] * kCz + cg * 8) * E;
+  }
   auto load_item = [&](Pos q) {
     if (q.r < p.n_rows && q.t0 + kPairs <= p.k_len) {
       bool valid;
       const int64_t base = pair_index(q.r, q.t0, valid);   // wave-uniform
+      const unsigned char *zb = zbytes + base * (kCz * E);
+      const uint8_t *mb = p.mask + base;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int64_t idx = base + poff[s];
-        raw[s].load(zbytes + (idx * kCz + cg * 8) * E);
-        mbyte[s] = p.mask[idx];
+        raw[s].load(zb + zoff[s]);
+        mbyte[s] = mb[poff[s]];
         mvalid[s] = true;
       }
     } else {
@@ -275,10 +282,15 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
   // staging rows -> HBM: one 16-byte piece per lane, whole 128-byte (bf16)
   // or 256-byte (fp32) channel rows per group of lanes.  The operand layout
   // keeps the 64 columns of an item contiguous within each channel block.
+  // (operand_offset is linear in the channel, and the 64 columns of an item
+  // are one contiguous run per channel: a wave-uniform base plus a
+  // loop-invariant lane offset)
+  constexpr int LPR = OUTB / 16;     // lanes per channel row
+  constexpr int RPI = 64 / LPR;      // rows per instruction
+  const uint32_t st_lane = (uint32_t)(lane / LPR) * (uint32_t)kOpBlock + (lane % LPR) * (16 / E);
   auto store_out = [&](Pos q) {
-    constexpr int LPR = OUTB / 16;     // lanes per channel row
-    constexpr int RPI = 64 / LPR;      // rows per instruction
     typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    T *const ob = out_plane + operand_offset(q.r, q.t0, c0, p.ld);   // wave-uniform
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int row = i * RPI + lane / LPR;
@@ -286,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       const u32x2 *src = reinterpret_cast<const u32x2 *>(stage + row * OSTR + piece * 16);
       const u32x2 lo = src[0], hi = src[1];
       if (active)
-        *reinterpret_cast<u32x4 *>(out_plane + operand_offset(q.r, q.t0, c0 + row, p.ld) + piece * (16 / E)) =
+        *reinterpret_cast<u32x4 *>(ob + (st_lane + (uint32_t)(i * RPI) * (uint32_t)kOpBlock)) =
             u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   };
