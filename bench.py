@@ -617,6 +617,56 @@ def cpu_baseline_epilogue_backward(work, wts, block=65536, blocks=4):
                       f"{n}x{n} grid would take {n * n / rate:.0f}s"}
 
 
+CONTRACTION_SHAPES = ((3605, 3605, 3605), (3584, 3456, 3605), (3584, 3605, 3605), (3605, 3456, 3605),
+                      (3840, 3840, 3605))
+
+
+def bench_contraction_shapes(args, dev):
+    """The contraction kernel alone (trimul_tile with one chunk, FIRST) on
+    rows x cols x k shapes around the n3605_4ch grid: the full grid, the same
+    grid cut to whole 256 x 384 tiles (3584 x 3456), each ragged edge alone,
+    and the grid padded to whole tiles (3840 x 3840).  Operands come from K1
+    on a seeded 3840-residue pair tensor; medians of HIP-event timings on the
+    launch stream.  The differences give what the ragged tile column and row
+    cost against their share of the work."""
+    import torch
+
+    import pair_representation_amd as pra
+    import workloads as wl
+
+    n = 3840
+    z = wl.make_pair_tensor(n, C_Z, 7, "bf16", dev)
+    mask = torch.ones((n, n), dtype=torch.uint8, device=dev)
+    w = pra.Weights(wl.make_weights(C_Z, C, 7, "bf16"), pra.BF16, device=dev)
+    res = []
+    for (m, nc, k) in CONTRACTION_SHAPES:
+        ld = (k + 63) // 64 * 64
+        a, b = pra.tile_operands(w, pra.OUTGOING, z, mask, 0, m, 0, nc, 0, k, ld)
+        x = pra.new_xacc(m, nc, dev)
+        ch = [(0, k, a, b)]
+        for _ in range(max(args.warmup, 1)):
+            pra.tile(w, n, 0, m, 0, nc, ch, pra.TILE_FIRST, x)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            pra.tile(w, n, 0, m, 0, nc, ch, pra.TILE_FIRST, x)
+            e[1].record()
+            evs.append(e)
+        torch.cuda.synchronize()
+        ts = sorted(e[0].elapsed_time(e[1]) for e in evs)
+        t = ts[len(ts) // 2] * 1e-3
+        fl = 2.0 * m * nc * k * C
+        res.append({"rows": m, "cols": nc, "k": k, "ms": t * 1e3, "TFLOP/s": fl / t / 1e12,
+                    "frac": fl / t / 1e12 / PEAK_BF16_TFLOPS})
+        log(f"[shapes] {m} x {nc} x {k}: {t * 1e3:.3f} ms, {fl / t / 1e12:.0f} TFLOP/s")
+        del a, b, x
+        torch.cuda.empty_cache()
+    return {"mode": "contraction-shapes", "metric": "contraction kernel time by tile shape", "dtype": "bf16",
+            "data": "synthetic (seeded 3840-residue pair tensor)", "steps": args.steps, "shapes": res}
+
+
 STREAM_MIXES = (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("k1_mix_1r_2w", 1, 2), ("k3_mix_3r_2w", 3, 2))
 
 
@@ -627,9 +677,11 @@ def bench_peaks(args, dev):
     kernels at the byte mixes of the projection (1 read : 2 written) and
     epilogue (3 : 2) kernels, plus plain read, write and copy; each streaming
     launch moves about 6 GiB (far beyond the 256 MB last-level cache) and is
-    run in four forms (plain or non-temporal accesses, 4 or 8 elements in
-    flight per thread) at several grid sizes, the best average reported.  Times are HIP
-    events on the launch stream."""
+    run as a grid-stride loop (plain or non-temporal accesses, 4 or 8
+    elements in flight per thread, 4 to 32 work-groups per CU) and in a
+    one-shot form (one element per thread over a covering grid, plain or
+    non-temporal), the best average reported per mix.  Times are HIP events
+    on the launch stream."""
     import ctypes
 
     import torch
@@ -692,28 +744,41 @@ def bench_peaks(args, dev):
             src.fill_(7)
         dst = torch.empty(w * units * 16, dtype=torch.uint8, device=dev) if w else None
         best = None
-        for variant in range(4):
-            for per_cu in (4, 8, 16, 32):
-                nb = cus * per_cu
+        forms = [(v, pc) for v in range(4) for pc in (4, 8, 16, 32)] + [(4, 0), (5, 0)]
+        for variant, per_cu in forms:
+            nb = cus * max(per_cu, 1)
 
-                def run():
-                    st = L.peaks_stream(r, w, variant, vp(src.data_ptr() if src is not None else 0),
-                                        vp(dst.data_ptr() if dst is not None else 0), units,
-                                        vp(u32sink.data_ptr()), nb, sp)
-                    if st != 0:
-                        raise RuntimeError(f"peaks_stream: hip error {st}")
+            def run():
+                st = L.peaks_stream(r, w, variant, vp(src.data_ptr() if src is not None else 0),
+                                    vp(dst.data_ptr() if dst is not None else 0), units,
+                                    vp(u32sink.data_ptr()), nb, sp)
+                if st != 0:
+                    raise RuntimeError(f"peaks_stream: hip error {st}")
 
-                tt = timed(run, 5)
-                gbs = (r + w) * units * 16 / tt / 1e9
-                if best is None or gbs > best["GB/s"]:
-                    best = {"GB/s": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "ms": tt * 1e3, "blocks": nb,
-                            "nontemporal": bool(variant & 1), "per_thread_step": 8 if variant & 2 else 4,
-                            "bytes_read": r * units * 16, "bytes_written": w * units * 16}
+            tt = timed(run, 5)
+            gbs = (r + w) * units * 16 / tt / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": gbs, "frac_of_8000": gbs / PEAK_HBM_GBS, "ms": tt * 1e3,
+                        "blocks": (units + 255) // 256 if variant >= 4 else nb,
+                        "form": "one element per thread" if variant >= 4 else
+                                f"{8 if variant & 2 else 4} elements per thread and step",
+                        "nontemporal": bool(variant & 1),
+                        "bytes_read": r * units * 16, "bytes_written": w * units * 16}
         res[name] = best
         log(f"[peaks] {name}: {best['GB/s']:.0f} GB/s ({best['blocks']} blocks)")
         del src, dst
         torch.cuda.empty_cache()
     out["stream"] = res
+    # the runtime's own device copy (torch copy_ -> HIP's copy kernel), for reference
+    nb = 3 << 30
+    a_t = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b_t = torch.empty_like(a_t)
+    tt = timed(lambda: b_t.copy_(a_t), 5)
+    out["runtime_copy"] = {"GB/s": 2 * nb / tt / 1e9, "frac_of_8000": 2 * nb / tt / 1e9 / PEAK_HBM_GBS,
+                           "ms": tt * 1e3, "bytes_read": nb, "bytes_written": nb}
+    log(f"[peaks] runtime copy: {out['runtime_copy']['GB/s']:.0f} GB/s")
+    del a_t, b_t
+    torch.cuda.empty_cache()
     return {"mode": "peaks", "metric": "achievable peaks (matrix-core loop, streaming kernels)", **out}
 
 
@@ -725,9 +790,10 @@ def main():
     ap.add_argument("--workload", default="n3605_4ch")
     ap.add_argument("--cpu-rows", type=int, default=256, help="row block for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "copy", "peaks", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
+                    choices=["bench", "copy", "peaks", "contraction-shapes", "backward", "epilogue-backward", "layer-backward", "atom-attention"],
                     help="copy: a plain 1 GiB device copy by the streaming probe kernel (counter calibration); "
                          "peaks: achievable matrix-core and streaming peaks (libtrimul_peaks.so); "
+                         "contraction-shapes: the contraction kernel on whole-tile and ragged shapes; "
                          "backward: the contraction step's gradients (trimul_tile_backward); "
                          "epilogue-backward: the epilogue's gradients (trimul_epilogue_backward); "
                          "layer-backward: every gradient of the layer (the three backward entry points); "
@@ -775,6 +841,9 @@ def main():
         return
     if args.mode == "peaks":
         print(json.dumps(bench_peaks(args, dev)), flush=True)
+        return
+    if args.mode == "contraction-shapes":
+        print(json.dumps(bench_contraction_shapes(args, dev)), flush=True)
         return
     work = wl.WORKLOADS[args.workload]
     if args.mode == "backward":

@@ -105,6 +105,21 @@ __global__ __launch_bounds__(256) void stream_rw(const u32x4 *__restrict__ src, 
   if (W == 0 && keep[0] == 0x9E3779B9u && keep[1] == 0x7F4A7C15u) sink[0] = keep[2];
 }
 
+// One-shot form: one element per thread, a grid that covers all elements
+// (no stride loop; the dispatcher places every work-group).
+template <int R, int W, bool NT>
+__global__ __launch_bounds__(256) void stream_once(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                   int64_t units, uint32_t *sink) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  u32x4 v = u32x4{(uint32_t)u, 1u, 2u, 3u};
+#pragma unroll
+  for (int r = 0; r < R; ++r) v ^= ld16<NT>(src + r * units + u);
+#pragma unroll
+  for (int w = 0; w < W; ++w) st16<NT>(dst + w * units + u, v + (uint32_t)w);
+  if (W == 0 && v[0] == 0x9E3779B9u && v[1] == 0x7F4A7C15u) sink[0] = v[2];
+}
+
 template <int R, int W, int U, bool NT>
 hipError_t launch_stream(const void *src, void *dst, int64_t units, uint32_t *sink, int blocks, hipStream_t s) {
   hipLaunchKernelGGL((stream_rw<R, W, U, NT>), dim3(blocks), dim3(256), 0, s, static_cast<const u32x4 *>(src),
@@ -112,11 +127,22 @@ hipError_t launch_stream(const void *src, void *dst, int64_t units, uint32_t *si
   return hipGetLastError();
 }
 
-// variant: bit 0 = non-temporal, bit 1 = 8 elements per thread and step (else 4)
+// variant: bit 0 = non-temporal, bit 1 = 8 elements per thread and step (else
+// 4); variants 4 and 5: the one-shot form (plain, non-temporal), whose grid
+// size follows from `units` (`blocks` is ignored)
 template <int R, int W>
 hipError_t launch_variant(int variant, const void *src, void *dst, int64_t units, uint32_t *sink, int blocks,
                           hipStream_t s) {
+  const int64_t once_blocks = (units + 255) / 256;
   switch (variant) {
+    case 4:
+      hipLaunchKernelGGL((stream_once<R, W, false>), dim3((unsigned)once_blocks), dim3(256), 0, s,
+                         static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), units, sink);
+      return hipGetLastError();
+    case 5:
+      hipLaunchKernelGGL((stream_once<R, W, true>), dim3((unsigned)once_blocks), dim3(256), 0, s,
+                         static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), units, sink);
+      return hipGetLastError();
     case 0: return launch_stream<R, W, 4, false>(src, dst, units, sink, blocks, s);
     case 1: return launch_stream<R, W, 4, true>(src, dst, units, sink, blocks, s);
     case 2: return launch_stream<R, W, 8, false>(src, dst, units, sink, blocks, s);
@@ -151,11 +177,13 @@ int peaks_mfma(int blocks, int iters, float *sink, unsigned long long *clk, void
 // each of `units` 16-byte elements (both pointers 16-byte aligned, src holding
 // r * units and dst w * units elements).  (r, w) in {(1,0), (0,1), (1,1),
 // (1,2), (3,2)}; variant 0..3 (bit 0 non-temporal, bit 1 eight elements per
-// thread and step).  Returns a hipError_t value.
+// thread and step), 4..5 one element per thread over a covering grid (plain,
+// non-temporal).  Returns a hipError_t value.
 int peaks_stream(int r, int w, int variant, const void *src, void *dst, long long units, uint32_t *sink,
                  int blocks, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (units <= 0 || blocks <= 0 || !sink || variant < 0 || variant > 3) return (int)hipErrorInvalidValue;
+  if (units <= 0 || blocks <= 0 || !sink || variant < 0 || variant > 5) return (int)hipErrorInvalidValue;
+  if (variant >= 4 && (units + 255) / 256 > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
   if ((r > 0 && !src) || (w > 0 && !dst)) return (int)hipErrorInvalidValue;
   if (r == 1 && w == 0) return (int)launch_variant<1, 0>(variant, src, dst, units, sink, blocks, s);
   if (r == 0 && w == 1) return (int)launch_variant<0, 1>(variant, src, dst, units, sink, blocks, s);
