@@ -178,8 +178,11 @@ size_t trimul_chunked_workspace_bytes(const trimul_weights_t *w, int64_t n, int6
  * fp32 accumulator, and after the last chunk the epilogue writes the tile
  * into out.  Besides z, mask and out, device memory is the workspace only
  * (trimul_chunked_workspace_bytes), independent of n when R, C and K are
- * fixed.  The a operand of a tile is rebuilt for every column tile and the b
- * operand for every row tile, so the projection work grows as n/C + n/R.
+ * fixed.  With K < n the a operand of a tile is rebuilt for every column
+ * tile and the b operand for every row tile, so the projection work grows as
+ * n/C + n/R passes over z; with K = n, a is built once per row tile (1 + n/R
+ * passes, b still rebuilt for every row tile), and with C = n as well b is
+ * built once per call (2 passes).
  * Arguments as trimul_outgoing plus dir and the three block sizes (>= 0;
  * 0 = n); errors as trimul_outgoing.  Results agree with trimul_outgoing /
  * trimul_incoming up to the fp32 summation order over k. */

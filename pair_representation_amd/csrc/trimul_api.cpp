@@ -307,12 +307,17 @@ trimul_status_t check_full_args(const trimul_weights_t *w, const void *z, const 
 // walked in chunks of K: the chunk's operands (K1), then the contraction
 // into the tile's accumulator (K2; the first chunk overwrites, the others
 // add), and after the last chunk the epilogue (K3) writes the tile straight
-// into out (row stride n).
+// into out (row stride n).  When one chunk covers all of k the buffers still
+// hold what a later tile needs: a (its rows, all of k) is kept across the
+// column blocks of a row block, and with a single column block b (all
+// columns, all of k) is built once for every row block.
 trimul_status_t enqueue_chunked(const trimul_weights_t *w, trimul_dir_t dir, const void *z, const uint8_t *mask,
                                 float *out, int64_t n, const ChunkedLayout &L, char *ws, hipStream_t s) {
   void *a_buf = ws + L.a_off;
   void *b_buf = ws + L.b_off;
   float *x = reinterpret_cast<float *>(ws + L.x_off);
+  const bool one_k = L.K >= n;
+  const bool one_c = L.C >= n;
   hipError_t e;
   for (int64_t r0 = 0; r0 < n; r0 += L.R) {
     const int64_t nr = std::min(L.R, n - r0);
@@ -320,8 +325,12 @@ trimul_status_t enqueue_chunked(const trimul_weights_t *w, trimul_dir_t dir, con
       const int64_t nc = std::min(L.C, n - c0);
       for (int64_t k0 = 0; k0 < n; k0 += L.K) {
         const int64_t kl = std::min(L.K, n - k0);
-        e = enqueue_operands(w, dir, z, mask, n, r0, nr, c0, nc, k0, kl, L.ldk, a_buf, b_buf, s);
-        if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        void *a_dst = (one_k && c0 > 0) ? nullptr : a_buf;
+        void *b_dst = (one_k && one_c && r0 > 0) ? nullptr : b_buf;
+        if (a_dst || b_dst) {
+          e = enqueue_operands(w, dir, z, mask, n, r0, nr, c0, nc, k0, kl, L.ldk, a_dst, b_dst, s);
+          if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        }
         trimul::K2Args k2{};
         k2.ch[0].a = a_buf;
         k2.ch[0].b = b_buf;

@@ -9,7 +9,8 @@ Bars (max |diff| / rms(ref)):
   k differs)                                                       <= 1e-4
 At N = 14000 the whole-grid entry point cannot run (its workspace alone is
 201 GB, with z and out 351 GB of the 288 GB); the chunked path runs in
-57 GB of workspace and is checked against the oracle on sampled pairs.
+88 GB of workspace (3584-row tiles, k in one chunk) or 57 GB (3500-row
+tiles, k in two chunks) and is checked against the oracle on sampled pairs.
 """
 
 import numpy as np
@@ -41,7 +42,8 @@ def _case(n, dtype, seed, dev):
 
 
 @pytest.mark.parametrize("direction", list(DIRS))
-@pytest.mark.parametrize("blocks", [(64, 0, 50), (100, 77, 128), (300, 300, 300), (257, 33, 299), (1, 300, 64)])
+@pytest.mark.parametrize("blocks", [(64, 0, 50), (100, 77, 128), (300, 300, 300), (257, 33, 299), (1, 300, 64),
+                                    (64, 77, 0), (64, 0, 0), (100, 300, 300)])
 def test_chunked_bf16_vs_oracle(dev, direction, blocks):
     n = 300
     R, C, K = blocks
@@ -81,7 +83,8 @@ def test_chunked_workspace_formula(dev):
         r = lambda v, m: (v + m - 1) // m * m
         return (a256(128 * r(R, 256) * r(K, 64) * e) + a256(128 * r(C, 256) * r(K, 64) * e)
                 + a256(128 * r(R, 4) * r(C, 16) * 4))
-    for n, R, C, K in ((5000, 512, 512, 512), (14000, 512, 512, 512), (14000, 3500, 0, 7000), (100, 0, 0, 0)):
+    for n, R, C, K in ((5000, 512, 512, 512), (14000, 512, 512, 512), (14000, 3500, 0, 7000), (14000, 3584, 0, 0),
+                       (100, 0, 0, 0)):
         R2, C2, K2 = (v if 0 < v <= n else n for v in (R, C, K))
         assert pra.chunked_workspace_bytes(w, n, R, C, K) == pieces(R2, C2, K2)
     with pytest.raises(pra.TrimulError):
@@ -90,15 +93,21 @@ def test_chunked_workspace_formula(dev):
 
 
 @pytest.mark.parametrize("direction", list(DIRS))
-def test_chunked_beyond_whole_grid_memory(dev, direction):
+@pytest.mark.parametrize("blocks", ["workload", (3500, 0, 7000)])
+def test_chunked_beyond_whole_grid_memory(dev, direction, blocks):
     """The n14000_chunked workload: the whole-grid path would need 351 GB with
-    z and out; the chunked path (3500-row tiles, full width, k in two chunks
-    of 7000) runs in z + out + 57 GB.  Checked on sampled pairs against the Q-oracle (rows
-    and columns at tile and chunk boundaries, first and last, random), plus
-    finiteness, exact zeros at masked pairs and the sample's rms."""
+    z and out; the chunked path runs in z + out + 88 GB with the workload's
+    blocks (3584-row tiles, full width, k in one chunk: each operand built
+    once) and in z + out + 57 GB with 3500-row tiles and k in two chunks of
+    7000 (operands rebuilt per tile and chunk).  Checked on sampled pairs
+    against the Q-oracle (rows and columns at tile and chunk boundaries, first
+    and last, random), plus finiteness, exact zeros at masked pairs and the
+    sample's rms."""
     work = wl.WORKLOADS["n14000_chunked"]
     n = work.n
-    R, C, K = work.chunked["row_block"], work.chunked["col_block"], work.chunked["k_block"]
+    if blocks == "workload":
+        blocks = (work.chunked["row_block"], work.chunked["col_block"], work.chunked["k_block"])
+    R, C, K = blocks
     print(f"[case] {work.name} {direction} blocks {(R, C, K)}", flush=True)
     free, total = torch.cuda.mem_get_info(dev)
     wts = wl.make_weights(work.c_z, work.c, work.seed, work.dtype)
@@ -115,7 +124,8 @@ def test_chunked_beyond_whole_grid_memory(dev, direction):
     torch.cuda.synchronize()
     print("  computed", flush=True)
     masked = np.flatnonzero(r == 0)[:4]
-    must = [3499, 3500, 6999, 7000, 10499, 10500, n - 1] + list(masked)
+    edges = sorted({e for b in (R, K) if 0 < b < n for m in range(b, n, b) for e in (m - 1, m)})
+    must = [0, n - 1] + edges + list(masked)
     rows = sample_indices(n, 61, count=24, must=must)
     cols = sample_indices(n, 62, count=24, must=must)
     gz, gm = device_getters(z, mask)

@@ -26,8 +26,9 @@ Workloads (sizes from the pages, values synthetic):
                      fit beside z and the output on one device (page 1's
                      "O problema dos workarounds atuais": chunking is the
                      single-GPU workaround); run in the memory-bounded form
-                     with 3500-row output blocks at full width and k in two
-                     chunks of 7000; 2% random residues masked out.
+                     with 3584-row output blocks (14 contraction tiles) at
+                     full width and k in one chunk, so both operands are
+                     built once; 2% random residues masked out.
 
 Every workload uses c_z = c = 128, z ~ N(0, 1), Xavier-normal weights (one
 draw per logical matrix), LayerNorm gamma = 1 and beta = 0.
@@ -80,7 +81,7 @@ WORKLOADS = {
                             tile={"row_off": 0, "n_rows": 5000, "col_off": 0, "n_cols": 5000,
                                   "chunk": 1250, "n_chunks": 8}),
     "n14000_chunked": Workload("n14000_chunked", 14000, "bf16", seed=6, masked_fraction=0.02,
-                               chunked={"row_block": 3500, "col_block": 0, "k_block": 7000}),
+                               chunked={"row_block": 3584, "col_block": 0, "k_block": 0}),
 }
 
 
