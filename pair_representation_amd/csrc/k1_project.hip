@@ -20,8 +20,11 @@
 //    in the same lanes, so the gated, masked product is formed in registers
 //    (bf16 weight fragments stay in registers for the whole pass);
 //  - one barrier per item.
-// Each lane ends up with 4 consecutive pairs of one channel, stored as one
-// 8-byte (bf16) or 16-byte (fp32) write.
+// Each lane ends up with 4 consecutive pairs of one channel; a wave stages
+// its 32 channel rows of the item in LDS and writes each as whole 128-byte
+// (bf16) lines, 16 bytes per lane.  z is read with non-temporal loads and
+// the operands are written with non-temporal stores: this kernel touches
+// neither again, and streaming them leaves the caches to other data.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,7 +42,9 @@ struct ZUnit;  // 8 channels of one pair as loaded from HBM
 template <>
 struct ZUnit<bf16_t> {
   u32x4 v;
-  __device__ __forceinline__ void load(const unsigned char *p) { v = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void load(const unsigned char *p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  }
   __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float (&f)[8]) const {
 #pragma unroll
@@ -298,8 +303,8 @@ __global__ __launch_bounds__(kThreads) void k1_project(K1Args p) {
       const u32x2 *src = reinterpret_cast<const u32x2 *>(stage + row * OSTR + piece * 16);
       const u32x2 lo = src[0], hi = src[1];
       if (active)
-        *reinterpret_cast<u32x4 *>(ob + (st_lane + (uint32_t)(i * RPI) * (uint32_t)kOpBlock)) =
-            u32x4{lo[0], lo[1], hi[0], hi[1]};
+        __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                                    reinterpret_cast<u32x4 *>(ob + (st_lane + (uint32_t)(i * RPI) * (uint32_t)kOpBlock)));
     }
   };
 

@@ -15,15 +15,18 @@
 //  - x: thread (pair p = tid % 32, channel group tid / 32) holds 16 channels;
 //    output LayerNorm statistics are combined over the 8 groups in LDS.
 //  - z is re-read (16 lanes per pair, 16-lane DPP reductions) and
-//    re-normalised for the gate.
+//    re-normalised for the gate.  x and z are read with non-temporal loads
+//    (each is read once here).
 //  - Both normalised operands go to LDS as matrix-core B operands; in bf16
 //    mode each is split into hi + lo bf16 terms (hi = bf16(v),
 //    lo = bf16(v - hi)) and multiplied by the bf16 weights twice, so the
 //    products keep fp32-level accuracy.
 //  - Wave w computes output channels 32*w .. +31 of both the projection
-//    and the gate for the item's 32 pairs, so the final product is formed in
-//    registers and stored from there, 16 bytes (4 channels) per lane.  bf16
-//    weight fragments stay in registers for the whole pass.
+//    and the gate for the item's 32 pairs (pairs as the rows of the
+//    products, channels as the columns), so the final product is formed in
+//    registers and stored from there, each store instruction writing whole
+//    128-byte lines (32 channels of two pairs).  bf16 weight fragments stay
+//    in registers for the whole pass.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,7 +47,9 @@ struct ZUnit;
 template <>
 struct ZUnit<bf16_t> {
   u32x4 v;
-  __device__ __forceinline__ void load(const unsigned char *p) { v = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void load(const unsigned char *p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  }
   __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float (&f)[8]) const {
 #pragma unroll
@@ -104,13 +109,14 @@ struct Operand<bf16_t> {
     f.zh.load(z + off);
     f.zl.load(z + PLANE + off);
   }
-  // ay += Wo * n, ag += Wg * z over 16 k values (both terms)
+  // ay += n * Wo^T, ag += z * Wg^T over 16 k values (both terms): pairs are
+  // the rows of the products, output channels the columns
   __device__ static void mma(f32x16 &ay, f32x16 &ag, const Frag<bf16_t> &wo, const Frag<bf16_t> &wg,
                              const Frags &f) {
-    ::trimul::mma(ay, wo, f.nh);
-    ::trimul::mma(ag, wg, f.zh);
-    ::trimul::mma(ay, wo, f.nl);
-    ::trimul::mma(ag, wg, f.zl);
+    ::trimul::mma(ay, f.nh, wo);
+    ::trimul::mma(ag, f.zh, wg);
+    ::trimul::mma(ay, f.nl, wo);
+    ::trimul::mma(ag, f.zl, wg);
   }
 };
 
@@ -132,8 +138,8 @@ struct Operand<float> {
   }
   __device__ static void mma(f32x16 &ay, f32x16 &ag, const Frag<float> &wo, const Frag<float> &wg,
                              const Frags &f) {
-    ::trimul::mma(ay, wo, f.n);
-    ::trimul::mma(ag, wg, f.z);
+    ::trimul::mma(ay, f.n, wo);
+    ::trimul::mma(ag, f.z, wg);
   }
 };
 
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) unsigned char n_ops[kOpBytes];   // normalised x
   __shared__ __attribute__((aligned(16))) unsigned char z_ops[kOpBytes];   // normalised z
   __shared__ __attribute__((aligned(8))) float2 part[kGroups][kPairs];    // per-group (mean, M2)
-  __shared__ __attribute__((aligned(4))) uint8_t mask_lds[kPairs];
+  __shared__ uint32_t mask_word;   // bit q: pair q of the item is kept
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // pair q at 4*jj + ii
     const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
 #pragma unroll
-    for (int c = 0; c < kXPer; ++c) xv[c] = xp[c * 64];
+    for (int c = 0; c < kXPer; ++c) xv[c] = __builtin_nontemporal_load(xp + c * 64);
     if (blk * 4 + kRows <= p.n_rows && s0 + kCols <= p.n_cols) {
       const int64_t base = (p.row_off + blk * 4) * p.n + p.col_off + s0;   // the item's first pair
 #pragma unroll
@@ -274,13 +280,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int c = 0; c < kXPer; ++c) { const float d = xv[c] - m; m2 += d * d; }
       part[grp][q] = make_float2(m, m2);
-      if (grp == 0) mask_lds[q] = (mvalid && mbyte != 0) ? 1 : 0;
+      // lanes q and q + 32 of wave 0 both hold pair q's mask byte
+      const uint64_t kept = __ballot(mvalid && mbyte != 0);
+      if (tid == 0) mask_word = (uint32_t)kept;
     }
     __syncthreads();   // (1)
-    // mask of this lane's output pair, read before (2): the next item's
-    // mask is written after it
-    const int pq = lane & 31;   // this lane's pair column
-    const bool keep = mask_lds[pq] != 0;
+    // the item's mask bits, read before (2): the next item's word is
+    // written after it
+    const uint32_t keep_bits = mask_word;
+    const int pq = lane & 31;   // pair of this lane's operand fragments
     {
       float2 pg[kGroups];
 #pragma unroll
@@ -346,24 +354,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     // ---- gate * projection * mask -> HBM ----------------------------------
-    // Accumulator registers 4g..4g+3 of a lane are 4 consecutive output
-    // channels of its pair: one 16-byte store each; the four stores of a lane
-    // and its partner lane (lane ^ 32) cover 32 consecutive channels (128
-    // bytes) of the pair's output row.
-    const int64_t r = blk * 4 + (pq & 3), col = s0 + (pq >> 2);
-    if (r < p.n_rows && col < p.n_cols) {
-      float *const orow = p.out + (r * p.out_ld + col) * kCz + o0;
+    // Accumulator register e of a lane is output channel o0 + lane % 32 of
+    // pair acc_row(e, lane) = 8 (e / 4) + 4 (lane / 32) + e % 4, i.e. row
+    // e % 4 and column 2 (e / 4) + lane / 32 of the item: for each register
+    // the two half-waves write the wave's 32 channels of one pair each, two
+    // whole 128-byte lines, so the stores bypass the caches (the output is
+    // not read again here) without partial-line writes.
+    const uint32_t kb = keep_bits >> (4 * (lane >> 5));
+    float *const obase = p.out + (blk * 4 * p.out_ld + s0 + (lane >> 5)) * kCz + o0 + (lane & 31);
+    const int64_t row_stride = p.out_ld * kCz;
+    const bool whole = blk * 4 + kRows <= p.n_rows && s0 + kCols <= p.n_cols;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g4 + i;
-          const float gated = sigmoid_of_exp2_arg(ag[e]) * ay[e];
-          v[i] = keep ? gated : 0.f;
-        }
-        *reinterpret_cast<f32x4 *>(orow + acc_row(4 * g4, lane)) = v;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int ii = e & 3, jj = 2 * (e >> 2) + (lane >> 5);
+      const float gated = sigmoid_of_exp2_arg(ag[e]) * ay[e];
+      const float v = ((kb >> (8 * (e >> 2) + (e & 3))) & 1u) ? gated : 0.f;
+      if (whole || (blk * 4 + ii < p.n_rows && s0 + jj < p.n_cols))
+        __builtin_nontemporal_store(v, obase + ii * row_stride + 2 * (e >> 2) * kCz);
     }
   }
 }
