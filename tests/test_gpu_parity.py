@@ -3,7 +3,14 @@ finishes in seconds, spanning several kernel tiles and ragged tails).
 
 Bars (max |diff| / rms(ref)):
   bf16 path vs the Q-mode oracle (bf16 contraction operands)  <= 1e-2
+  bf16 path vs the exact oracle                                <= 5e-2
   fp32 path vs the exact oracle                                <= 1e-4
+The second bar bounds what the bf16 contraction operands themselves cost:
+rounding the normalised pair rows and a, b to bf16 (and nothing else) moves
+the exact result by 1.6e-2 to 3.3e-2 of its rms at the sizes below (the
+Q-mode oracle against the exact one, on the CPU), so no bf16 path meets
+1e-2 against the exact oracle; the GPU path must add no more than its own
+fp32-level error on top.
 The kernel-level tests are tighter: the contraction kernel alone, fed the
 oracle's own bf16 operands, must match their float64 contraction to fp32
 accumulation error.
@@ -21,6 +28,7 @@ from tests.gpu_util import device_getters, rel_err
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 1e-2
+BF16_EXACT_TOL = 5e-2
 F32_TOL = 1e-4
 DIRS = ("outgoing", "incoming")
 
@@ -64,6 +72,7 @@ def test_full_bf16(dev, direction, n):
     assert np.all(np.isfinite(got))
     assert np.all(got[h["mask"] == 0] == 0.0)
     assert e <= BF16_TOL
+    assert e_exact <= BF16_EXACT_TOL
 
 
 @pytest.mark.parametrize("direction", DIRS)
