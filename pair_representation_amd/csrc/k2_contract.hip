@@ -168,25 +168,43 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   // last 32-row block holding a valid row (see the edge-tile skipping below)
   const int a_rows = row_extent((int)(p.M - m0), BM);
   const int b_rows = row_extent((int)(p.N - n0), BN);
-  auto issue_loads = [&](int ci, int kt, int buf) __attribute__((always_inline)) {
+  // The chunk whose k-tiles are being loaded, kept in registers: this
+  // tile's operand blocks at the chunk's first k-tile, the distance between
+  // 256-row blocks and the chunk's k-tile count.  Refreshed from the kernel
+  // arguments only when the next chunk starts, so the k-loop issues no
+  // scalar memory loads (which would also make every LDS wait a full one).
+  const unsigned char *a_chunk = nullptr, *b_chunk = nullptr;
+  int64_t blk_step = 0;
+  int chunk_kt = 0;
+  auto set_chunk = [&](int ci) __attribute__((always_inline)) {
+    const K2Chunk &ch = p.ch[ci];
+    const int64_t col_blocks = (int64_t)((uint64_t)ch.ld / kOpCols);   // ld: a positive multiple of 64
+    blk_step = col_blocks * kC * kOpBlock * C::E;
+    a_chunk = static_cast<const unsigned char *>(ch.a) +
+              ((int64_t)(m0 / kOpRows) * col_blocks * kC + d) * kOpBlock * C::E;
+    b_chunk = static_cast<const unsigned char *>(ch.b) +
+              ((int64_t)(n0 / kOpRows) * col_blocks * kC + d) * kOpBlock * C::E;
+    chunk_kt = ch.ktiles;
+  };
+  // Loads of k-tile kt of the current chunk into LDS stage buf.  With
+  // `full` (every row of both operand tiles valid) no load is tested.
+  auto issue_loads = [&](int kt, int buf, auto full) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full)::value;
+    if (wave >= kLoadWaves) return;
     // The k-tile is one contiguous run of one channel block of each operand
     // (256 rows x 64 columns per block; a BK-wide k-tile is columns kk ..
-    // kk+BK-1 of it, rows m0 % 256 ..).
-    const int64_t ld = p.ch[ci].ld;
-    const int64_t kcol = (int64_t)kt * BK;
-    const int64_t cb = kcol / kOpCols;
-    const int kk = (int)(kcol % kOpCols);
+    // kk+BK-1 of it, rows m0 % 256 ..); channel blocks of consecutive column
+    // blocks are kC blocks apart.
+    const int kcol = kt * BK;
+    const int64_t cb_off = (int64_t)(kcol / kOpCols) * kC * kOpBlock * C::E;
+    const int kk = kcol % kOpCols;
     // An A tile lies in one 256-row block; a B tile (384 rows) in at most
     // two consecutive ones.  Each 8-row load group lies in one block and is
     // addressed through that block's own buffer descriptor.
-    const int64_t blk_step = (ld / kOpCols) * kC * kOpBlock * C::E;   // bytes between 256-row blocks
-    const int64_t a_blk = ((int64_t)(m0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
-    const int64_t b_blk = ((int64_t)(n0 / kOpRows) * (ld / kOpCols) + cb) * kC + d;
-    const unsigned char *A = static_cast<const unsigned char *>(p.ch[ci].a) + a_blk * kOpBlock * C::E;
-    const unsigned char *B = static_cast<const unsigned char *>(p.ch[ci].b) + b_blk * kOpBlock * C::E;
+    const unsigned char *A = a_chunk + cb_off;
+    const unsigned char *B = b_chunk + cb_off;
     unsigned char *sa = lds + buf * C::STAGE;
     unsigned char *sb = sa + BM * C::ROWB;
-    if (wave >= kLoadWaves) return;
     // Load instruction i of this wave covers tile rows 32*i + 8*wave .. +7,
     // i.e. rows r0 + 32*i + 8*wave of the first block: with r0 (the tile's
     // first row inside its block, 0 or 128) a compile-time constant, the
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int q = i * kLoadWaves + wave;
-        if (q * 8 >= valid_rows) continue;   // rows only skipped blocks would read
+        if (!kFull && q * 8 >= valid_rows) continue;   // rows only skipped blocks would read
         constexpr int kBlockRows = kOpRows;
         const bool upper = r0 + 32 * i >= kBlockRows;   // folded per unrolled i
         const int r = (r0 + q * 8) % kBlockRows;
@@ -234,11 +252,18 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
 
   int ci = 0, kt = 0;  // position of the next k-tile to load
   auto advance = [&]() {
-    if (++kt == p.ch[ci].ktiles) { ++ci; kt = 0; }
+    if (++kt == chunk_kt) {
+      ++ci;
+      kt = 0;
+      if (ci < p.n_chunks) set_chunk(ci);
+    }
   };
 
+  using F = std::false_type;
+  using Tr = std::true_type;
   if (total_kt > 0) {
-    issue_loads(ci, kt, 0);
+    set_chunk(0);
+    issue_loads(kt, 0, F{});
     advance();
     wait_vm0();
     __syncthreads();
@@ -316,10 +341,10 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
       if (!kRollA) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto k_loop = [&](auto mta, auto nta, auto checked) __attribute__((always_inline)) {
+  auto k_loop = [&](auto mta, auto nta, auto checked, auto loads_full) __attribute__((always_inline)) {
     for (int it = 0; it + 1 < total_kt; ++it) {
       const int buf = it & 1;
-      issue_loads(ci, kt, buf ^ 1);
+      issue_loads(kt, buf ^ 1, loads_full);
       advance();
       compute(buf, mta, nta, checked);
       wait_vm0();
@@ -336,22 +361,26 @@ __global__ __launch_bounds__(kThreads) void k2_contract(K2Args p) {
   //    column blocks 1 or NT, a count in between rounded up (the extra blocks
   //    lie inside the tile, multiply stale LDS rows and are never written);
   //    the checked loop is slow when edge waves keep most of their blocks.
-  using F = std::false_type;
-  using Tr = std::true_type;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using IM = std::integral_constant<int, C::MT>;
   using IN = std::integral_constant<int, C::NT>;
   if constexpr (C::MT * C::NT > 8) {
-    if (mt_act == C::MT && nt_act == C::NT) k_loop(IM{}, IN{}, F{});
-    else k_loop(IM{}, IN{}, Tr{});
+    // tiles whose operand rows are all valid also load without tests
+    const bool loads_full = a_rows >= BM && b_rows >= BN;
+    if (mt_act == C::MT && nt_act == C::NT) {
+      if (loads_full) k_loop(IM{}, IN{}, F{}, Tr{});
+      else k_loop(IM{}, IN{}, F{}, F{});
+    } else {
+      k_loop(IM{}, IN{}, Tr{}, F{});
+    }
   } else {
     auto k_loop_n = [&](auto mta) __attribute__((always_inline)) {
-      if (nt_act == 1) k_loop(mta, I1{}, F{});
-      else k_loop(mta, IN{}, F{});
+      if (nt_act == 1) k_loop(mta, I1{}, F{}, F{});
+      else k_loop(mta, IN{}, F{}, F{});
     };
-    if (mt_act == 0 || nt_act == 0) k_loop(I0{}, I0{}, F{});   // loads and barriers only
+    if (mt_act == 0 || nt_act == 0) k_loop(I0{}, I0{}, F{}, F{});   // loads and barriers only
     else if (mt_act == 1) k_loop_n(I1{});
     else if (mt_act == 2) k_loop_n(std::conditional_t<(C::MT > 2), I2, IM>{});
     else k_loop_n(IM{});
