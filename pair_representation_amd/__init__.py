@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, without the ``trimul_`` prefix):
     chunked_workspace_bytes(w, n, row_block, col_block, k_block)
     forward_chunked(z, mask, w, direction, row_block, col_block, k_block, ...)
     forward_chunked_noalloc(z, mask, w, direction, row_block, col_block, k_block, out=None)
+    plan_chunked(w, n, budget_bytes)   (host helper: blocks whose workspace fits a budget)
     tile_operand_bytes(w, rows, ld)
     tile_operands(w, direction, z, mask, row_off, n_rows, col_off, n_cols, k_off, k_len, ld, ...)
     tile(w, n, row_off, n_rows, col_off, n_cols, chunks, flags, x_acc, z, mask, out_tile)
@@ -269,6 +270,35 @@ def forward_chunked(z, mask, w: Weights, direction: int, row_block: int = 0, col
     _check(lib().trimul_forward_chunked(w.ref, direction, _ptr(z), _ptr(mask), _ptr(out), n, row_block, col_block,
                                         k_block, _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def plan_chunked(w: Weights, n: int, budget_bytes: int):
+    """Blocks (row_block, col_block, k_block) for forward_chunked whose
+    workspace fits in ``budget_bytes``, in order of preference: k in one
+    chunk at full width (each operand built once; the tallest row tile that
+    fits, in multiples of 256 rows), then k in chunks at full width, then
+    square tiles.  Sizes come from chunked_workspace_bytes; raises
+    ValueError when not even 256 x 256 x 256 blocks fit."""
+    if n < 1:
+        raise ValueError("n must be positive")
+
+    def fits(r, c, k):
+        return chunked_workspace_bytes(w, n, r, c, k) <= budget_bytes
+
+    rows = sorted({n} | set(range(256, n, 256)), reverse=True)
+    for r in rows:
+        if fits(r, 0, 0):
+            return (0 if r >= n else r, 0, 0)
+    ks = [k for k in (n // 2, n // 4, n // 8, 1024, 512, 256) if 64 <= k < n]
+    for k in sorted({(k + 63) // 64 * 64 for k in ks}, reverse=True):
+        for r in rows:
+            if fits(r, 0, k):
+                return (0 if r >= n else r, 0, k)
+    for b in (4096, 2048, 1024, 512, 256):
+        b = min(b, n)
+        if fits(b, b, b):
+            return (b, b, b)
+    raise ValueError(f"no blocks fit a workspace of {budget_bytes} bytes at n={n}")
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20   # TRIMUL_NOALLOC_SCRATCH_BYTES

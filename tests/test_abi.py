@@ -12,6 +12,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import pair_representation_amd as pra
 
@@ -467,3 +468,25 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(pra, "LIB_PATH", "/nonexistent/libtrimul.so")
     with pytest.raises(RuntimeError, match="missing"):
         pra.lib()
+
+
+def test_plan_chunked_picks_fitting_blocks():
+    """plan_chunked: the tallest full-width row tile with k in one chunk that
+    fits the budget, else chunks of k, else square tiles; never a workspace
+    beyond the budget."""
+    mats = {k: torch.zeros(128, 128) for k in pra.Weights.MATRICES}
+    vecs = {k: torch.zeros(128) for k in pra.Weights.VECTORS}
+    w = pra.Weights({**mats, **vecs}, pra.BF16, device="cpu")
+    n = 14000
+    # a 288 GiB device holding z, mask and out, with 4 GiB to spare
+    budget = (288 << 30) - n * n * (128 * 2 + 1 + 128 * 4) - (4 << 30)
+    R, C, K = pra.plan_chunked(w, n, budget)
+    assert (C, K) == (0, 0) and R % 256 == 0 and 0 < R < n
+    assert pra.chunked_workspace_bytes(w, n, R, C, K) <= budget
+    assert pra.chunked_workspace_bytes(w, n, R + 256, 0, 0) > budget
+    small = pra.chunked_workspace_bytes(w, n, 512, 512, 512)
+    R, C, K = pra.plan_chunked(w, n, small)
+    assert pra.chunked_workspace_bytes(w, n, R, C, K) <= small
+    assert pra.plan_chunked(w, 300, 1 << 40) == (0, 0, 0)
+    with pytest.raises(ValueError):
+        pra.plan_chunked(w, n, 1000)

@@ -93,7 +93,7 @@ def test_chunked_workspace_formula(dev):
 
 
 @pytest.mark.parametrize("direction", list(DIRS))
-@pytest.mark.parametrize("blocks", ["workload", (3500, 0, 7000)])
+@pytest.mark.parametrize("blocks", ["workload", (3500, 0, 7000), "planned"])
 def test_chunked_beyond_whole_grid_memory(dev, direction, blocks):
     """The n14000_chunked workload: the whole-grid path would need 351 GB with
     z and out; the chunked path runs in z + out + 88 GB with the workload's
@@ -102,17 +102,21 @@ def test_chunked_beyond_whole_grid_memory(dev, direction, blocks):
     7000 (operands rebuilt per tile and chunk).  Checked on sampled pairs
     against the Q-oracle (rows and columns at tile and chunk boundaries, first
     and last, random), plus finiteness, exact zeros at masked pairs and the
-    sample's rms."""
+    sample's rms.  A third case takes the blocks plan_chunked picks for the
+    device's free memory."""
     work = wl.WORKLOADS["n14000_chunked"]
     n = work.n
-    if blocks == "workload":
-        blocks = (work.chunked["row_block"], work.chunked["col_block"], work.chunked["k_block"])
-    R, C, K = blocks
-    print(f"[case] {work.name} {direction} blocks {(R, C, K)}", flush=True)
     free, total = torch.cuda.mem_get_info(dev)
     wts = wl.make_weights(work.c_z, work.c, work.seed, work.dtype)
     w = pra.Weights(wts, pra.BF16, device=dev)
     io = n * n * (128 * 2 + 1 + 128 * 4)                  # z, mask, out
+    if blocks == "workload":
+        blocks = (work.chunked["row_block"], work.chunked["col_block"], work.chunked["k_block"])
+    elif blocks == "planned":
+        # the tallest tiles the free memory allows beside z, mask and out (2 GiB kept back)
+        blocks = pra.plan_chunked(w, n, free - io - (2 << 30))
+    R, C, K = blocks
+    print(f"[case] {work.name} {direction} blocks {(R, C, K)}", flush=True)
     need = io + pra.chunked_workspace_bytes(w, n, R, C, K)
     # the whole-grid path cannot hold its workspace beside z and out here
     assert io + pra.workspace_bytes(w, n) > total
