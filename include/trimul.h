@@ -182,7 +182,8 @@ size_t trimul_chunked_workspace_bytes(const trimul_weights_t *w, int64_t n, int6
  * tile and the b operand for every row tile, so the projection work grows as
  * n/C + n/R passes over z; with K = n, a is built once per row tile (1 + n/R
  * passes, b still rebuilt for every row tile), and with C = n as well b is
- * built once per call (2 passes).
+ * built once per call (2 passes; 2 - R/n when R is a multiple of 256, the
+ * first tile's a and b then coming from one pass).
  * Arguments as trimul_outgoing plus dir and the three block sizes (>= 0;
  * 0 = n); errors as trimul_outgoing.  Results agree with trimul_outgoing /
  * trimul_incoming up to the fp32 summation order over k. */

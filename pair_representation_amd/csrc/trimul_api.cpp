@@ -327,7 +327,17 @@ trimul_status_t enqueue_chunked(const trimul_weights_t *w, trimul_dir_t dir, con
         const int64_t kl = std::min(L.K, n - k0);
         void *a_dst = (one_k && c0 > 0) ? nullptr : a_buf;
         void *b_dst = (one_k && one_c && r0 > 0) ? nullptr : b_buf;
-        if (a_dst || b_dst) {
+        if (one_k && one_c && r0 == 0 && nr < n && nr % 256 == 0) {
+          // First row tile, b built once at full width: a and b of the
+          // tile's rows in one projection pass, then b of the other rows.
+          // Those start on a 256-row operand block, so that part of the b
+          // buffer is an operand buffer of its own.
+          e = enqueue_operands(w, dir, z, mask, n, 0, nr, 0, nr, 0, kl, L.ldk, a_buf, b_buf, s);
+          if (e == hipSuccess)
+            e = enqueue_operands(w, dir, z, mask, n, 0, 0, nr, n - nr, 0, kl, L.ldk, nullptr,
+                                 static_cast<char *>(b_buf) + operand_bytes(nr, L.ldk, w->dtype), s);
+          if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        } else if (a_dst || b_dst) {
           e = enqueue_operands(w, dir, z, mask, n, r0, nr, c0, nc, k0, kl, L.ldk, a_dst, b_dst, s);
           if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
         }

@@ -43,7 +43,7 @@ def _case(n, dtype, seed, dev):
 
 @pytest.mark.parametrize("direction", list(DIRS))
 @pytest.mark.parametrize("blocks", [(64, 0, 50), (100, 77, 128), (300, 300, 300), (257, 33, 299), (1, 300, 64),
-                                    (64, 77, 0), (64, 0, 0), (100, 300, 300)])
+                                    (64, 77, 0), (64, 0, 0), (100, 300, 300), (256, 0, 0)])
 def test_chunked_bf16_vs_oracle(dev, direction, blocks):
     n = 300
     R, C, K = blocks
