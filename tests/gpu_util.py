@@ -15,15 +15,19 @@ def rel_err(got, ref):
 def device_getters(z_dev, mask_dev):
     """get_z / get_mask callables for the oracle's sampled evaluation that copy
     the requested rows x cols of device tensors to the host."""
+    def pick(t, ri, ci):
+        # the smaller index set first, so the intermediate copy stays small
+        ri_t = torch.as_tensor(np.asarray(ri), device=t.device, dtype=torch.long)
+        ci_t = torch.as_tensor(np.asarray(ci), device=t.device, dtype=torch.long)
+        if len(ri_t) <= len(ci_t):
+            return t.index_select(0, ri_t).index_select(1, ci_t)
+        return t.index_select(1, ci_t).index_select(0, ri_t)
+
     def get_z(ri, ci):
-        ri_t = torch.as_tensor(np.asarray(ri), device=z_dev.device, dtype=torch.long)
-        ci_t = torch.as_tensor(np.asarray(ci), device=z_dev.device, dtype=torch.long)
-        return z_dev.index_select(0, ri_t).index_select(1, ci_t).to(torch.float64).cpu().numpy()
+        return pick(z_dev, ri, ci).to(torch.float64).cpu().numpy()
 
     def get_mask(ri, ci):
-        ri_t = torch.as_tensor(np.asarray(ri), device=mask_dev.device, dtype=torch.long)
-        ci_t = torch.as_tensor(np.asarray(ci), device=mask_dev.device, dtype=torch.long)
-        return mask_dev.index_select(0, ri_t).index_select(1, ci_t).cpu().numpy()
+        return pick(mask_dev, ri, ci).cpu().numpy()
 
     return get_z, get_mask
 

@@ -148,3 +148,42 @@ def test_n10000_tile_sampled(dev, direction):
     _whole_tensor_checks(out, mask[:t["n_rows"], :t["n_cols"]], ref, gm(rows, cols))
     del z, mask, chunks, x, out
     _free()
+
+
+def test_whole_grid_near_device_limit(dev):
+    """The whole-grid entry points at the largest N (a multiple of 256) whose
+    workspace fits beside z, mask and out in the device's free memory (8 GiB
+    kept back): both directions on a 24 x 24 sample of residues (first, last,
+    masked, random) against the Q-oracle, plus whole-tensor checks."""
+    _free()
+    free, _ = torch.cuda.mem_get_info(dev)
+    wts = wl.make_weights(128, 128, 11, "bf16")
+    w, w64 = pra.Weights(wts, pra.BF16, device=dev), wl.weights_f64(wts)
+    io = lambda m: m * m * (128 * 2 + 1 + 128 * 4)
+    n = 256
+    while io(n + 256) + pra.workspace_bytes(w, n + 256) <= free - (8 << 30):
+        n += 256
+    work = wl.Workload("n_device_limit", n, "bf16", seed=11, masked_fraction=0.02)
+    print(f"[case] whole grid at n={n} ({(io(n) + pra.workspace_bytes(w, n)) / 1e9:.0f} GB of "
+          f"{free / 1e9:.0f} GB free)", flush=True)
+    assert n >= 4096
+    z, mask, _ = wl.make_inputs(work, dev)
+    masked = list(np.flatnonzero(wl.residue_mask(work) == 0)[:4])
+    rows = sample_indices(n, 111, 24, masked)
+    cols = sample_indices(n, 222, 24, masked[::-1])
+    gz, gm = device_getters(z, mask)
+    ws = pra.new_workspace(w, n, dev)
+    for direction in ("outgoing", "incoming"):
+        fn = pra.outgoing if direction == "outgoing" else pra.incoming
+        out = fn(z, mask, w, workspace=ws)
+        torch.cuda.synchronize()
+        got = out[torch.as_tensor(rows, device=dev)][:, torch.as_tensor(cols, device=dev)].double().cpu().numpy()
+        ref = oracle.trimul_sampled(gz, gm, n, w64, direction, rows, cols, quant=True)
+        e = rel_err(got, ref)
+        print(f"  {direction}: sampled {len(rows)}x{len(cols)} vs Q-oracle {e:.3e}", flush=True)
+        assert e <= BF16_TOL
+        _whole_tensor_checks(out, mask, ref, gm(rows, cols))
+        del out
+        _free()
+    del z, mask, ws
+    _free()
