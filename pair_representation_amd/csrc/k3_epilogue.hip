@@ -364,13 +364,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float *const obase = p.out + (blk * 4 * p.out_ld + s0 + (lane >> 5)) * kCz + o0 + (lane & 31);
     const int64_t row_stride = p.out_ld * kCz;
     const bool whole = blk * 4 + kRows <= p.n_rows && s0 + kCols <= p.n_cols;
+    if (whole && keep_bits == 0xffffffffu) {
+      // an item wholly inside the tile with every pair kept
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int ii = e & 3, jj = 2 * (e >> 2) + (lane >> 5);
-      const float gated = sigmoid_of_exp2_arg(ag[e]) * ay[e];
-      const float v = ((kb >> (8 * (e >> 2) + (e & 3))) & 1u) ? gated : 0.f;
-      if (whole || (blk * 4 + ii < p.n_rows && s0 + jj < p.n_cols))
-        __builtin_nontemporal_store(v, obase + ii * row_stride + 2 * (e >> 2) * kCz);
+      for (int e = 0; e < 16; ++e) {
+        const int ii = e & 3;
+        __builtin_nontemporal_store(sigmoid_of_exp2_arg(ag[e]) * ay[e],
+                                    obase + ii * row_stride + 2 * (e >> 2) * kCz);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ii = e & 3, jj = 2 * (e >> 2) + (lane >> 5);
+        const float gated = sigmoid_of_exp2_arg(ag[e]) * ay[e];
+        const float v = ((kb >> (8 * (e >> 2) + (e & 3))) & 1u) ? gated : 0.f;
+        if (whole || (blk * 4 + ii < p.n_rows && s0 + jj < p.n_cols))
+          __builtin_nontemporal_store(v, obase + ii * row_stride + 2 * (e >> 2) * kCz);
+      }
     }
   }
 }
