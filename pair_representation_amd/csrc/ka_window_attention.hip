@@ -11,7 +11,9 @@
 // Work-group = one (sequence, window), 4 waves; wave v takes heads v, v+4, ...
 // (two waves per SIMD: the register budget is held to 256 per lane).  Per
 // head, all global loads (Q, K, the bias row, V) are issued before any use, so
-// a head costs one memory round trip.
+// a head costs one memory round trip; the first head's are issued together
+// with the window's key-mask bytes, ahead of the barrier that publishes the
+// key flags, so a work-group with one head per wave waits for memory once.
 // Per head, on the matrix cores (bf16 32x32x16, fp32 accumulation):
 //  - S^T = K Q^T for the 4 key blocks of 32: lane l holds query l % 32 and 16
 //    keys of each block, so a query's 128 logits sit in two lanes (l, l ^ 32):
@@ -21,7 +23,8 @@
 //  - O = P V with the normalised probabilities as A operand straight from the
 //    S^T registers: key block b, step s takes accumulator registers 8s .. 8s+7
 //    of lane (q, half), i.e. keys 32b + 16 half + 8s .. +7; the B operand reads
-//    the same keys of V from a transposed LDS copy (one 16-byte read).  P is
+//    the same keys of V from a transposed per-wave LDS copy (one 16-byte
+//    read; the copy is written four keys of one dimension per 8-byte store).  P is
 //    split into hi + lo bf16 terms (two products per step), so the output
 //    keeps about 16 significant bits of P.
 // Key validity (inside the sequence and unmasked) is computed once per
@@ -51,20 +54,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t b = wg / p.n_windows, w = wg % p.n_windows;
   const int64_t key0 = kQ * w + kKOff;
   const int q = lane & 31, hl = lane >> 5;
-  // Row r of a 32-key block of S^T stands for key 16 ((r >> 2) & 1) + 4 (r >> 3)
-  // + (r & 3): the 16 rows a lane holds (acc_row(e, l), e = 0..15) are then
-  // keys 16 (l / 32) + e, so the lane's bias, key flags and V operands are
-  // contiguous runs.
-  const int kperm = 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
   const int64_t n = p.n_atoms;
-
-  if (threadIdx.x < kK) {
-    const int64_t j = key0 + threadIdx.x;
-    bool ok = j >= 0 && j < n;
-    if (ok && p.mask) ok = p.mask[b * n + j] != 0;
-    key_ok[threadIdx.x] = ok ? 1 : 0;
-  }
-  __syncthreads();
 
   const bf16_t *Q = static_cast<const bf16_t *>(p.q);
   const bf16_t *Kp = static_cast<const bf16_t *>(p.k);
@@ -78,40 +68,81 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
   const float sl = p.scale * kLog2e;
   uint16_t *const myvt = vt[wave];
 
+  // A head's operands in registers: Q (B operand over d), K (A operand, 4
+  // key blocks), this lane's bias row pieces, and V rows for the LDS copy.
+  Frag<bf16_t> qf[2], kf[4][2];
+  u32x4 braw[4][2];   // keys 32 bb + 16 hl + 8 j .. +7 of this lane's query
+  u32x4 vraw[kK / 16];
+  auto load_head = [&](int64_t h) {
+    // The lane index passes through an opaque copy, so the lane-dependent
+    // addresses are recomputed per head instead of being kept live across
+    // the head loop (which would exceed the register budget).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lq = ln & 31, lh = ln >> 5;
+    // Row r of a 32-key block of S^T stands for key kperm(r) = 16 ((r >> 2) & 1)
+    // + 4 (r >> 3) + (r & 3): the 16 rows a lane holds (acc_row(e, l),
+    // e = 0..15) are then keys 16 (l / 32) + e, so the lane's bias, key flags
+    // and V operands are contiguous runs.
+    const int kperm = 16 * ((lq >> 2) & 1) + 4 * (lq >> 3) + (lq & 3);
+    const int64_t qi = kQ * w + lq;
+    const int64_t qrow = row(qi < n ? qi : n - 1, h);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * lh);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int64_t krow = row(clampj(key0 + 32 * bb + kperm), h);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) kf[bb][ks].load(Kp + krow + 16 * ks + 8 * lh);
+    }
+    const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + lq) * kK : nullptr;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        braw[bb][j] = brow ? *reinterpret_cast<const u32x4 *>(brow + 32 * bb + 16 * lh + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    // V: lane -> keys 64 (it / 4) + 4 (l / 4) + it % 4, dims 8 (l % 4) .. +7
+#pragma unroll
+    for (int it = 0; it < kK / 16; ++it)
+      vraw[it] = *reinterpret_cast<const u32x4 *>(
+          V + row(clampj(key0 + 64 * (it >> 2) + 4 * (ln >> 2) + (it & 3)), h) + 8 * (ln & 3));
+  };
+
+  // Key flags (inside the sequence and unmasked), once per work-group.  The
+  // mask bytes are requested first and the first head's operands right after,
+  // so both arrive within one memory round trip.
+  bool jin = false;
+  uint8_t mbyte = 1;
+  if (threadIdx.x < kK) {
+    const int64_t j = key0 + threadIdx.x;
+    jin = j >= 0 && j < n;
+    if (jin && p.mask) mbyte = p.mask[b * n + j];
+  }
+  if (wave < H) load_head(wave);
+  if (threadIdx.x < kK) key_ok[threadIdx.x] = (jin && mbyte != 0) ? 1 : 0;
+  __syncthreads();
+
   // Each wave owns its V^T copy, so no work-group barrier is needed inside the
   // loop: the wave's LDS operations execute in order, and compiler barriers
   // keep the copy's writes before its reads and this head's reads before the
   // next head's writes.  All global loads of a head are issued first.
   for (int64_t h = wave; h < H; h += kWaves) {
-    // ---- loads: Q (B operand over d), K (A operand, 4 key blocks), bias, V
-    Frag<bf16_t> qf[2], kf[4][2];
-    const int64_t qi = kQ * w + q;
-    const int64_t qrow = row(qi < n ? qi : n - 1, h);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[ks].load(Q + qrow + 16 * ks + 8 * hl);
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int64_t krow = row(clampj(key0 + 32 * bb + kperm), h);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kf[bb][ks].load(Kp + krow + 16 * ks + 8 * hl);
-    }
-    const bf16_t *brow = Bias ? Bias + (((b * p.n_windows + w) * H + h) * kQ + q) * kK : nullptr;
-    u32x4 braw[4][2];   // keys 32 bb + 16 hl + 8 j .. +7 of this lane's query
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        braw[bb][j] = brow ? *reinterpret_cast<const u32x4 *>(brow + 32 * bb + 16 * hl + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-    // ---- V^T of the window into LDS: lane -> key 16 it + l / 4, dims 8 (l % 4) .. +7
+    // ---- loads (the first head's were issued before the key-flag barrier)
+    if (h != wave) load_head(h);
+    // ---- V^T of the window into LDS
     asm volatile("" ::: "memory");   // the previous head's V^T reads stay before these writes
+    // (four consecutive keys of one dimension per 8-byte store)
 #pragma unroll
-    for (int it = 0; it < kK / 16; ++it) {
-      const int t = 16 * it + (lane >> 2), c = lane & 3;
-      const u32x4 v4 = *reinterpret_cast<const u32x4 *>(V + row(clampj(key0 + t), h) + 8 * c);
+    for (int half = 0; half < 2; ++half) {
+      const int t = 64 * half + 4 * (lane >> 2), c = lane & 3;
+      const u32x4 *v4 = vraw + 4 * half;   // keys t .. t+3
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        myvt[(8 * c + 2 * m) * kVtStride + t] = (uint16_t)(v4[m] & 0xffffu);
-        myvt[(8 * c + 2 * m + 1) * kVtStride + t] = (uint16_t)(v4[m] >> 16);
+      for (int i = 0; i < 4; ++i) {
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+        const u32x2 even{(v4[0][i] & 0xffffu) | (v4[1][i] << 16), (v4[2][i] & 0xffffu) | (v4[3][i] << 16)};
+        const u32x2 odd{(v4[0][i] >> 16) | (v4[1][i] & 0xffff0000u), (v4[2][i] >> 16) | (v4[3][i] & 0xffff0000u)};
+        *reinterpret_cast<u32x2 *>(myvt + (8 * c + 2 * i) * kVtStride + t) = even;
+        *reinterpret_cast<u32x2 *>(myvt + (8 * c + 2 * i + 1) * kVtStride + t) = odd;
       }
     }
     asm volatile("" ::: "memory");   // the writes stay before the reads below
