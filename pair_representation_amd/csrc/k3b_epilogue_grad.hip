@@ -467,6 +467,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     // the next item's loads (this item's are all consumed)
     if (tile + 1 < tile_end) load_item(nxt);
+    // projection mode: this item's rows of the global dz are read here, so
+    // that the read-modify-write at the end of the item finds them in
+    // registers (each pair's row is touched by one item of one launch only)
+    f32x4 dz_old[4];
+    if constexpr (kProj) {
+      if (in_tile) {
+        const float *const dzr = p.dz + pair_of(blk * 4 + (q & 3), s0 + (q >> 2)) * kCz + o0 + 4 * hl;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) dz_old[g4] = *reinterpret_cast<const f32x4 *>(dzr + 8 * g4);
+      }
+    }
     __syncthreads();   // (3)
 
     // ---- G += dy x^T, H += dt z^T over the item's 32 pairs -----------------
@@ -564,7 +575,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         float *const dzrow = p.dz + pair_of(r, col) * kCz + o0 + 4 * hl;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 vz = *reinterpret_cast<const f32x4 *>(dzrow + 8 * g4);
+          f32x4 vz = dz_old[g4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int k = o0 + acc_row(4 * g4 + i, lane);
