@@ -310,7 +310,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   auto pair_of = [&](int64_t r, int64_t c) -> int64_t {
     return p.transposed ? (p.col_off + c) * p.n + p.row_off + r : (p.row_off + r) * p.n + p.col_off + c;
   };
-  auto load_item = [&](const Pos &ps) {
+  // x, z and the mask byte (consumed before the second barrier of an item)
+  auto load_xz = [&](const Pos &ps) {
     if constexpr (!kProj) {
       const float *xp = p.x + x_offset(ps.blk * 4, ps.s0, c0, p.ldx) + q;
 #pragma unroll
@@ -323,6 +324,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int64_t g = pair_of(rr, cc);
     zr.load(zbytes + (g * kCz + c0) * E);
     mbyte = p.mask[g];
+  };
+  // dL/dout (consumed when dy and dt are formed)
+  auto load_dout = [&](const Pos &ps) {
+    const int64_t r = ps.blk * 4 + (q & 3), col = ps.s0 + (q >> 2);
+    const int64_t rr = r < p.n_rows ? r : p.n_rows - 1;
+    const int64_t cc = col < p.n_cols ? col : p.n_cols - 1;
     if constexpr (kProj) {
       // the x layout: channel o of position (r, c) at x_offset(r, c, o) (the
       // item's block exists in the buffer, padding included)
@@ -336,6 +343,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) dv[g4] = *reinterpret_cast<const f32x4 *>(dp + 8 * g4);
     }
+  };
+  auto load_item = [&](const Pos &ps) {
+    load_xz(ps);
+    load_dout(ps);
   };
 
   f32x16 G[4], H[4];
@@ -423,6 +434,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     __syncthreads();   // (2)
+    // the next item's x, z and mask (this item's are consumed)
+    if (tile + 1 < tile_end) load_xz(nxt);
 
     // ---- accumulator layout: recompute y and the gate --------------------
     f32x16 a0, a1;   // y = W_y n and -log2(e) t, then dn and dzh
@@ -465,8 +478,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       Op::put4(dy_ops, q, o0 + 8 * g4 + 4 * hl, fy);
       Op::put4(dt_ops, q, o0 + 8 * g4 + 4 * hl, ft);
     }
-    // the next item's loads (this item's are all consumed)
-    if (tile + 1 < tile_end) load_item(nxt);
+    // the next item's dL/dout (this item's is consumed)
+    if (tile + 1 < tile_end) load_dout(nxt);
     // projection mode: this item's rows of the global dz are read here, so
     // that the read-modify-write at the end of the item finds them in
     // registers (each pair's row is touched by one item of one launch only)
