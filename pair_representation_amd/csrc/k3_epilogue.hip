@@ -222,14 +222,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     zoff[s] = (pr & 3) * (int)p.n + (pr >> 2);
   }
   const int moff = (q & 3) * (int)p.n + (q >> 2);
-  auto load_item = [&](const Pos &ps) {
-    const int64_t blk = ps.blk, s0 = ps.s0;
-    // x: the item is one half (8 columns) of a 4 x 16 block of the x layout
-    // (x_offset): 128 channels x 32 pairs, 128 contiguous bytes per channel,
-    // pair q at 4*jj + ii
-    const float *xp = p.x + x_offset(blk * 4, s0, xc0, p.ldx) + q;
+  // x: the item is one half (8 columns) of a 4 x 16 block of the x layout
+  // (x_offset): 128 channels x 32 pairs, 128 contiguous bytes per channel,
+  // pair q at 4*jj + ii
+  auto load_x = [&](const Pos &ps) {
+    const float *xp = p.x + x_offset(ps.blk * 4, ps.s0, xc0, p.ldx) + q;
 #pragma unroll
     for (int c = 0; c < kXPer; ++c) xv[c] = __builtin_nontemporal_load(xp + c * 64);
+  };
+  // z and the mask byte
+  auto load_zm = [&](const Pos &ps) {
+    const int64_t blk = ps.blk, s0 = ps.s0;
     if (blk * 4 + kRows <= p.n_rows && s0 + kCols <= p.n_cols) {
       const int64_t base = (p.row_off + blk * 4) * p.n + p.col_off + s0;   // the item's first pair
 #pragma unroll
@@ -246,6 +249,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       mbyte = p.mask[pair_index(blk, s0, q, valid)];
       mvalid = valid;
     }
+  };
+  auto load_item = [&](const Pos &ps) {
+    load_x(ps);
+    load_zm(ps);
   };
 
   // Each work-group takes a contiguous range of work items, so consecutive
@@ -311,6 +318,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
+    // the next item's x (this item's is consumed): requested ahead of z and
+    // the mask, so the prefetch goes out in two bursts
+    if (tile + 1 < tile_end) load_x(nxt);
+
     // ---- input LayerNorm of z (recomputed) for the gate --------------------
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -330,8 +341,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();   // (2)
 
-    // ---- prefetch the next item ----------------------------------------------
-    if (tile + 1 < tile_end) load_item(nxt);
+    // ---- prefetch the rest of the next item --------------------------------
+    if (tile + 1 < tile_end) load_zm(nxt);
 
     // ---- projections on the matrix cores ----------------------------------
     f32x16 ay, ag;
